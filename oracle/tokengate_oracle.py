@@ -1,0 +1,176 @@
+"""Float64 CPU oracle for TokenGate's gated-prefill path.
+
+TEST INFRASTRUCTURE ONLY.  This module is the independent checker of the HIP
+path: only the test-suite, the smoke check and the benchmark's CPU-baseline leg
+may import or run it.  It shares no code with the HIP library and imports
+nothing from the product package.  Every function is a plain, slow, literal
+statement of what the TokenGate pages define, in float64 NumPy.
+
+Sources (pages are cited by site and title; sections by their headings):
+  [P1] aiproducthub.cn, "斯坦福伯克利TokenGate 预填充提速11.3倍", section 事件详情
+  [P2] aisight.pl, "TokenGate: Stanford i Berkeley ucza model, ktore tokeny
+       pominac przy czytaniu dlugiego kontekstu", section "Jak to dziala"
+  [P4] news.chathome.org TokenGate article, sections
+       "TokenGate の学習可能なトークンプルーニングの仕組み" and
+       "トークンゲート付きアテンションとは"
+
+The pages give the method in words only.  The formula of the gated attention
+logit, q.k / (sqrt(d) tau) + g_h s_j under a causal mask on original positions,
+is the specification this build adopts for those words.  Readings taken where
+the pages are silent are listed with each function.
+
+Parity status: every function here is pinned by CPU tests against library
+routines (torch's GELU / normal CDF, Linear layers and scaled_dot_product_attention
+in float64), brute-force sorting, tabulated normal-CDF values and invariants.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import erf as _erf
+
+__all__ = [
+    "gelu", "gate_score", "num_kept", "select_topk", "gather_kept",
+    "gated_attention", "causal_attention",
+]
+
+
+# ----------------------------------------------------------------------------------------
+# (1) gate scorer  [P1 事件详情; P2 "Jak to dziala"; P4 仕組み]
+# A small MLP maps each token's post-attention residual at the gate layer to one
+# scalar score.  Form d_model -> d_hidden -> 1 with a GELU between the layers.
+# Reading: "GELU" is the exact one, x * Phi(x) with Phi the standard normal CDF
+# (not the tanh approximation).  b1 and b2 are optional (zero in the workloads).
+# ----------------------------------------------------------------------------------------
+def gelu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0)))
+
+
+def gate_score(x, w1, b1, w2, b2=0.0):
+    """s[i] = b2 + sum_j w2[j] * GELU(b1[j] + sum_k x[i,k] * w1[j,k]).
+
+    x: [N, d_model]; w1: [d_hidden, d_model] (output-by-input layout);
+    b1: [d_hidden] or None; w2: [d_hidden]; b2: scalar.  Returns float64 [N].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w1 = np.asarray(w1, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    h = x @ w1.T
+    if b1 is not None:
+        h = h + np.asarray(b1, dtype=np.float64)[None, :]
+    a = gelu(h)
+    return a @ w2 + float(b2)
+
+
+# ----------------------------------------------------------------------------------------
+# (2) top-K selection over the document only  [P1 事件详情; P2 "Jak to dziala"; P4 仕組み]
+# Only the document part of the prompt can be pruned; the question is always kept.
+# Of the document tokens, the K highest-scoring ones are kept.  Kept tokens are
+# listed in ascending original position ("stable position order").
+# Readings: K counts document tokens only and is clamped to D = doc_end - doc_begin;
+# ties go to the lower position; -0 equals +0; NaN ranks below every number
+# (including -inf), ties among NaNs again to the lower position.
+# ----------------------------------------------------------------------------------------
+def num_kept(n, doc_begin, doc_end, k):
+    d = doc_end - doc_begin
+    return (n - d) + min(k, d)
+
+
+def select_topk(scores, doc_begin, doc_end, k):
+    """Kept positions (int64, ascending): every non-document position plus the
+    min(k, D) best document positions, found through the K-th largest value."""
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    if not (0 <= doc_begin <= doc_end <= n) or k < 0:
+        raise ValueError("bad selection arguments")
+    d = doc_end - doc_begin
+    k_eff = min(k, d)
+    pos = np.arange(doc_begin, doc_end, dtype=np.int64)
+    vals = s[doc_begin:doc_end]
+    is_nan = np.isnan(vals)
+    num_pos, num_vals = pos[~is_nan], vals[~is_nan]
+    nan_pos = pos[is_nan]
+
+    if k_eff <= len(num_vals):
+        if k_eff == 0:
+            chosen = np.zeros(0, dtype=np.int64)
+        else:
+            # threshold t = the k_eff-th largest number; keep everything above it,
+            # then fill the remaining quota from the values equal to t, lowest
+            # positions first.
+            t = np.partition(num_vals, len(num_vals) - k_eff)[len(num_vals) - k_eff]
+            above = num_pos[num_vals > t]
+            need = k_eff - len(above)
+            at_t = num_pos[num_vals == t]          # already ascending
+            chosen = np.concatenate([above, at_t[:need]])
+    else:
+        # every number is kept; NaNs fill the rest, lowest positions first
+        chosen = np.concatenate([num_pos, nan_pos[:k_eff - len(num_vals)]])
+
+    outside = np.concatenate([np.arange(0, doc_begin, dtype=np.int64),
+                              np.arange(doc_end, n, dtype=np.int64)])
+    return np.sort(np.concatenate([outside, chosen]).astype(np.int64))
+
+
+# ----------------------------------------------------------------------------------------
+# (3) gather  [P1 事件详情; P2 "Jak to dziala"; P4 仕組み]
+# Layers above the gate process only the kept tokens; pruned tokens create no
+# KV entries.  The kept rows (and their scores) are compacted in position order.
+# ----------------------------------------------------------------------------------------
+def gather_kept(x, scores, kept):
+    kept = np.asarray(kept, dtype=np.int64)
+    return np.asarray(x)[kept], np.asarray(scores)[kept]
+
+
+# ----------------------------------------------------------------------------------------
+# (4) token-gated attention  [P1 事件详情; P2 "Jak to dziala"; P4 トークンゲート付きアテンションとは]
+# Each kept key's score becomes a bias on the attention logits above the gate,
+# scaled by a learnable per-head gain; a learnable temperature corrects for each
+# query seeing fewer keys.  Adopted form:
+#     logit[i, j] = q_i . k_j / (sqrt(d) * tau) + gain[h] * s_kept[j],   pos_j <= pos_i
+# Readings: tau scales the q.k term only; gain is per query head; grouped-query
+# heads share key/value head g(h) = h // (Hq / Hkv); question tokens carry their
+# own score as bias like every kept key; s_kept=None or gain=None turns the bias off.
+# ----------------------------------------------------------------------------------------
+def gated_attention(q, k, v, pos, s_kept, gain, tau, rows=None, block=512):
+    """q: [M, Hq, d]; k, v: [M, Hkv, d]; pos: [M] original positions.
+    Returns float64 [len(rows), Hq, d] (all rows when rows is None)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    if hq % hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = hq // hkv
+    rows = np.arange(m, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    use_bias = s_kept is not None and gain is not None
+    if use_bias:
+        s_kept = np.asarray(s_kept, dtype=np.float64)
+        gain = np.asarray(gain, dtype=np.float64)
+    scale = 1.0 / (math.sqrt(d) * float(tau))
+    out = np.empty((len(rows), hq, d), dtype=np.float64)
+    for r0 in range(0, len(rows), block):
+        rb = rows[r0:r0 + block]
+        visible = pos[None, :] <= pos[rb][:, None]          # [b, M]
+        for h in range(hq):
+            g = h // group
+            logits = (q[rb, h, :] @ k[:, g, :].T) * scale
+            if use_bias:
+                logits = logits + gain[h] * s_kept[None, :]
+            logits = np.where(visible, logits, -np.inf)
+            mx = logits.max(axis=1, keepdims=True)
+            p = np.exp(logits - mx)
+            p /= p.sum(axis=1, keepdims=True)
+            out[r0:r0 + len(rb), h, :] = p @ v[:, g, :]
+    return out
+
+
+def causal_attention(q, k, v, rows=None):
+    """Ordinary causal grouped-query attention: the gated form with the bias off,
+    tau = 1 and positions 0..M-1."""
+    m = np.asarray(q).shape[0]
+    return gated_attention(q, k, v, np.arange(m), None, None, 1.0, rows=rows)

@@ -1,0 +1,321 @@
+"""Pins of the float64 oracle against things other than itself.
+
+Each check uses an independent source: tabulated normal-CDF values, torch's own
+GELU / Linear / scaled_dot_product_attention in float64, brute-force full sorts,
+a scalar textbook attention loop, and invariants of the definitions.  The cases
+are chosen so that a dropped term (bias, gain, temperature, b1, b2), a wrong sign,
+a wrong head mapping or a transposed operand fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.filterwarnings("ignore::UserWarning")
+
+
+def _table(golden_dir):
+    rows = []
+    with open(os.path.join(golden_dir, "normal_cdf.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                x, p = line.split()
+                rows.append((float(x), float(p)))
+    return rows
+
+
+# --------------------------------------------------------------------------- GELU
+def test_gelu_matches_tabulated_normal_cdf(golden_dir):
+    for x, phi in _table(golden_dir):
+        assert oracle.gelu(x) == pytest.approx(x * phi, abs=1e-15)
+        assert oracle.gelu(-x) == pytest.approx(-x * (1.0 - phi), abs=1e-15)
+
+
+def test_gelu_matches_torch_exact_gelu_and_ndtr():
+    x = np.random.default_rng(1).normal(scale=4.0, size=2000)
+    xt = torch.from_numpy(x)
+    ref = torch.nn.functional.gelu(xt, approximate="none").numpy()
+    np.testing.assert_allclose(oracle.gelu(x), ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.gelu(x), (xt * torch.special.ndtr(xt)).numpy(), rtol=0, atol=1e-13)
+
+
+def test_gelu_limits_and_odd_part():
+    assert oracle.gelu(0.0) == 0.0
+    assert oracle.gelu(40.0) == 40.0
+    assert abs(oracle.gelu(-40.0)) < 1e-300
+    x = np.linspace(-6, 6, 97)
+    # GELU(x) - GELU(-x) = x  (Phi(x) + Phi(-x) = 1)
+    np.testing.assert_allclose(oracle.gelu(x) - oracle.gelu(-x), x, atol=1e-14)
+
+
+# --------------------------------------------------------------------------- scorer
+def test_gate_score_matches_torch_mlp():
+    g = np.random.default_rng(2)
+    n, d, h = 37, 24, 10
+    x = g.normal(size=(n, d))
+    w1 = g.normal(size=(h, d)) / math.sqrt(d)
+    b1 = g.normal(size=h)
+    w2 = g.normal(size=h)
+    b2 = 0.37
+    lin1 = torch.nn.Linear(d, h, dtype=torch.float64)
+    lin2 = torch.nn.Linear(h, 1, dtype=torch.float64)
+    with torch.no_grad():
+        lin1.weight.copy_(torch.from_numpy(w1))
+        lin1.bias.copy_(torch.from_numpy(b1))
+        lin2.weight.copy_(torch.from_numpy(w2[None, :]))
+        lin2.bias.fill_(b2)
+        ref = lin2(torch.nn.GELU()(lin1(torch.from_numpy(x))))[:, 0].numpy()
+    np.testing.assert_allclose(oracle.gate_score(x, w1, b1, w2, b2), ref, rtol=0, atol=1e-12)
+
+
+def test_gate_score_one_hot_reads_table_values(golden_dir):
+    # w1 row j is the unit vector e_{perm[j]} (non-square: d_model=6, d_hidden=4),
+    # so h[i, j] = x[i, perm[j]] + b1[j]; w2 = e_j2 picks one hidden unit.
+    table = [(x, p) for x, p in _table(golden_dir) if x > 0]
+    perm = [4, 0, 5, 2]
+    d, hdim = 6, 4
+    w1 = np.zeros((hdim, d))
+    for j, c in enumerate(perm):
+        w1[j, c] = 1.0
+    b1 = np.array([0.25, -0.5, 0.5, 1.0])
+    b2 = -0.125
+    j2 = 2                           # hidden unit 2 reads column 5, bias +0.5
+    w2 = np.zeros(hdim)
+    w2[j2] = 1.0
+    x = np.zeros((len(table), d))
+    for i, (xv, _) in enumerate(table):
+        x[i, perm[j2]] = xv - b1[j2]          # h = xv exactly
+        x[i, perm[0]] = 7.0                   # other units must not leak in
+    s = oracle.gate_score(x, w1, b1, w2, b2)
+    expect = np.array([xv * p for xv, p in table]) + b2
+    np.testing.assert_allclose(s, expect, rtol=0, atol=1e-15)
+    # negative side: h = -xv -> GELU = -xv * (1 - Phi(xv))
+    x2 = np.zeros((len(table), d))
+    for i, (xv, _) in enumerate(table):
+        x2[i, perm[j2]] = -xv - b1[j2]
+    s2 = oracle.gate_score(x2, w1, b1, w2, 0.0)
+    np.testing.assert_allclose(s2, np.array([-xv * (1 - p) for xv, p in table]), rtol=0, atol=1e-15)
+
+
+def test_gate_score_linear_in_w2_and_b2():
+    g = np.random.default_rng(3)
+    x = g.normal(size=(9, 8)); w1 = g.normal(size=(5, 8))
+    wa, wb = g.normal(size=5), g.normal(size=5)
+    sa = oracle.gate_score(x, w1, None, wa, 0.0)
+    sb = oracle.gate_score(x, w1, None, wb, 0.0)
+    np.testing.assert_allclose(oracle.gate_score(x, w1, None, 2 * wa - 3 * wb, 1.5), 2 * sa - 3 * sb + 1.5,
+                               atol=1e-12)
+
+
+# --------------------------------------------------------------------------- selection
+def _brute_force(s, b, e, k):
+    """Full sort of the document by (score desc, position asc), NaN last."""
+    doc = list(range(b, e))
+    def key(i):
+        v = s[i]
+        return (1, 0.0, i) if math.isnan(v) else (0, -v, i)
+    top = sorted(doc, key=key)[:min(k, e - b)]
+    return sorted(set(range(0, b)) | set(range(e, len(s))) | set(top))
+
+
+def _random_scores(g, n):
+    kind = g.integers(0, 4)
+    if kind == 0:
+        return g.normal(size=n)
+    if kind == 1:       # heavy ties
+        return g.integers(-3, 4, size=n).astype(np.float64)
+    if kind == 2:       # signed zeros, infinities and NaNs mixed with ties
+        pool = np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, np.nan, 2.5])
+        return pool[g.integers(0, len(pool), size=n)]
+    return np.full(n, 0.5)  # all equal
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_select_matches_brute_force_sort(seed):
+    g = np.random.default_rng(100 + seed)
+    n = int(g.integers(1, 40))
+    b = int(g.integers(0, n + 1)); e = int(g.integers(b, n + 1))
+    s = _random_scores(g, n)
+    d = e - b
+    for k in sorted({0, 1, max(d - 1, 0), d, d + 5, int(g.integers(0, d + 1))}):
+        got = oracle.select_topk(s, b, e, k)
+        assert got.tolist() == _brute_force(s, b, e, k), (s, b, e, k)
+        assert len(got) == oracle.num_kept(n, b, e, k)
+
+
+def test_select_invariants_on_tiny_workload():
+    from learned_token_pruning_scorer_amd import configs, inputs
+    w = configs.WORKLOADS["tiny"]
+    gi = inputs.gate_inputs(w)
+    s = oracle.gate_score(inputs.to_f64(gi.x, w.dtype), inputs.to_f64(gi.w1, w.dtype), gi.b1,
+                          inputs.to_f64(gi.w2, w.dtype), gi.b2)
+    k = w.budgets[0]
+    kept = oracle.select_topk(s, w.doc_begin, w.doc_end, k)
+    assert len(kept) == w.n_kept(k)
+    assert np.all(np.diff(kept) > 0)
+    doc_kept = kept[(kept >= w.doc_begin) & (kept < w.doc_end)]
+    assert len(doc_kept) == min(k, w.n_doc)
+    assert set(range(w.doc_end, w.n)) <= set(kept.tolist())
+    dropped = np.setdiff1d(np.arange(w.doc_begin, w.doc_end), doc_kept)
+    assert s[doc_kept].min() >= s[dropped].max()
+    t = s[doc_kept].min()
+    tied_kept, tied_dropped = doc_kept[s[doc_kept] == t], dropped[s[dropped] == t]
+    if len(tied_dropped):
+        assert tied_kept.max() < tied_dropped.min()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_select_nested_across_budgets(seed):
+    g = np.random.default_rng(200 + seed)
+    n = 300
+    s = g.integers(-20, 20, size=n).astype(np.float64) / 4.0
+    prev = set(oracle.select_topk(s, 10, 280, 0).tolist())
+    for k in range(1, 275, 7):
+        cur = set(oracle.select_topk(s, 10, 280, k).tolist())
+        assert prev <= cur
+        prev = cur
+
+
+def test_select_rejects_bad_spans():
+    with pytest.raises(ValueError):
+        oracle.select_topk(np.zeros(4), 3, 2, 1)
+    with pytest.raises(ValueError):
+        oracle.select_topk(np.zeros(4), 0, 5, 1)
+    with pytest.raises(ValueError):
+        oracle.select_topk(np.zeros(4), 0, 4, -1)
+
+
+# --------------------------------------------------------------------------- gather
+def test_gather_is_row_indexing():
+    g = np.random.default_rng(4)
+    x = g.normal(size=(11, 3)); s = g.normal(size=11)
+    kept = np.array([0, 2, 3, 7, 10])
+    xk, sk = oracle.gather_kept(x, s, kept)
+    assert xk.tolist() == [x[i].tolist() for i in kept]
+    assert sk.tolist() == [s[i] for i in kept]
+
+
+# --------------------------------------------------------------------------- attention
+def _sdpa_reference(q, k, v, pos, s_kept, gain, tau):
+    """torch SDPA in float64 with an additive mask = bias + causal(-inf on positions)."""
+    m, hq, d = q.shape
+    group = hq // k.shape[1]
+    qt = torch.from_numpy(q).permute(1, 0, 2)                       # [Hq, M, d]
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(group, dim=0)
+    pos_t = torch.from_numpy(np.asarray(pos, dtype=np.int64))
+    mask = torch.zeros(hq, m, m, dtype=torch.float64)
+    if s_kept is not None:
+        mask += torch.from_numpy(np.asarray(gain, np.float64))[:, None, None] * \
+            torch.from_numpy(np.asarray(s_kept, np.float64))[None, None, :]
+    mask = mask.masked_fill(pos_t[None, :] > pos_t[:, None], float("-inf"))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=mask, scale=1.0 / (math.sqrt(d) * tau))
+    return out.permute(1, 0, 2).numpy()
+
+
+def _attn_case(seed, m=37, hq=4, hkv=2, d=16):
+    g = np.random.default_rng(seed)
+    q = g.normal(size=(m, hq, d)); k = g.normal(size=(m, hkv, d)); v = g.normal(size=(m, hkv, d))
+    s = g.normal(size=m) * 2.0
+    gain = g.uniform(0.5, 1.5, size=hq)
+    pos = np.sort(g.choice(4 * m, size=m, replace=False))
+    return q, k, v, pos, s, gain
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (4, 4), (6, 2), (3, 1)])
+def test_attention_matches_torch_sdpa_with_bias_mask(hq, hkv):
+    q, k, v, pos, s, gain = _attn_case(5 + hq + hkv, hq=hq, hkv=hkv)
+    tau = 1.3
+    got = oracle.gated_attention(q, k, v, pos, s, gain, tau)
+    ref = _sdpa_reference(q, k, v, pos, s, gain, tau)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_attention_unbiased_tau1_is_textbook_causal_sdpa():
+    q, k, v, _, _, _ = _attn_case(6)
+    m, hq, d = q.shape
+    got = oracle.causal_attention(q, k, v)
+    kt = torch.from_numpy(k).permute(1, 0, 2).repeat_interleave(2, dim=0)
+    vt = torch.from_numpy(v).permute(1, 0, 2).repeat_interleave(2, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).permute(1, 0, 2), kt, vt, is_causal=True).permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_attention_scalar_loop_tiny():
+    # scalar textbook evaluation: M=5, Hq=2, Hkv=1, d=3, gapped positions
+    q, k, v, pos, s, gain = _attn_case(7, m=5, hq=2, hkv=1, d=3)
+    tau = 0.8
+    got = oracle.gated_attention(q, k, v, pos, s, gain, tau)
+    for i in range(5):
+        for h in range(2):
+            logits = []
+            for j in range(5):
+                if pos[j] <= pos[i]:
+                    dot = sum(q[i, h, c] * k[j, 0, c] for c in range(3))
+                    logits.append((j, dot / (math.sqrt(3) * tau) + gain[h] * s[j]))
+            top = max(val for _, val in logits)
+            w = [(j, math.exp(val - top)) for j, val in logits]
+            z = sum(e for _, e in w)
+            for c in range(3):
+                ref = sum(e * v[j, 0, c] for j, e in w) / z
+                assert got[i, h, c] == pytest.approx(ref, abs=1e-13)
+
+
+def test_attention_invariants():
+    q, k, v, pos, s, gain = _attn_case(8)
+    tau = 1.1
+    base = oracle.gated_attention(q, k, v, pos, s, gain, tau)
+    # adding a constant to every kept score only shifts each row's logits
+    np.testing.assert_allclose(oracle.gated_attention(q, k, v, pos, s + 3.7, gain, tau), base, atol=1e-12)
+    # (Q, tau) == (Q / tau, 1)
+    np.testing.assert_allclose(oracle.gated_attention(q / tau, k, v, pos, s, gain, 1.0), base, atol=1e-12)
+    # the first kept row sees only itself
+    np.testing.assert_allclose(base[0], np.repeat(v[0], 2, axis=0), atol=1e-15)
+    # masking on positions equals masking on the row index when positions ascend
+    np.testing.assert_allclose(oracle.gated_attention(q, k, v, np.arange(len(pos)), s, gain, tau), base,
+                               atol=1e-15)
+    # a sampled subset of rows equals the same rows of the full evaluation
+    rows = np.array([0, 5, 17, 36])
+    np.testing.assert_allclose(oracle.gated_attention(q, k, v, pos, s, gain, tau, rows=rows), base[rows],
+                               atol=1e-15)
+
+
+def test_attention_bias_direction_and_gain_per_query_head():
+    q, k, v, pos, s, gain = _attn_case(9, m=12, hq=4, hkv=2, d=8)
+    s2 = np.zeros_like(s)
+    s2[3] = 60.0                       # one key dominates through its score
+    gain2 = np.array([1.0, 0.0, 1.0, 0.0])
+    out = oracle.gated_attention(q, k, v, pos, s2, gain2, 1.0)
+    for i in range(3, 12):
+        np.testing.assert_allclose(out[i, 0], v[3, 0], atol=1e-12)   # head 0 -> kv head 0
+        np.testing.assert_allclose(out[i, 2], v[3, 1], atol=1e-12)   # head 2 -> kv head 1
+    # gain 0 on heads 1 and 3: identical to the unbiased attention there
+    unb = oracle.gated_attention(q, k, v, pos, None, None, 1.0)
+    np.testing.assert_allclose(out[:, 1], unb[:, 1], atol=1e-12)
+    np.testing.assert_allclose(out[:, 3], unb[:, 3], atol=1e-12)
+    # a negative score pushes weight away from its key
+    s3 = np.zeros_like(s); s3[0] = -60.0
+    out3 = oracle.gated_attention(q, k, v, pos, s3, np.ones(4), 1.0)
+    ref = oracle.gated_attention(q[1:], k[1:], v[1:], pos[1:], None, None, 1.0)
+    np.testing.assert_allclose(out3[1:], ref, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- pipeline
+def test_full_budget_unbiased_pipeline_equals_causal_attention():
+    g = np.random.default_rng(10)
+    n, dm, hdim = 40, 12, 6
+    x = g.normal(size=(n, dm)); w1 = g.normal(size=(hdim, dm)); w2 = g.normal(size=hdim)
+    s = oracle.gate_score(x, w1, None, w2, 0.0)
+    kept = oracle.select_topk(s, 0, 32, 32 + 3)
+    assert kept.tolist() == list(range(n))
+    _, s_kept = oracle.gather_kept(x, s, kept)
+    q = g.normal(size=(n, 2, 4)); k = g.normal(size=(n, 1, 4)); v = g.normal(size=(n, 1, 4))
+    np.testing.assert_allclose(oracle.gated_attention(q, k, v, kept, s_kept, np.zeros(2), 1.0),
+                               oracle.causal_attention(q, k, v), atol=1e-14)
