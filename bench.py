@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Throughput of the TokenGate gated-prefill hot path on one MI355X.
+
+One step = the whole path over one prompt already resident in HBM:
+    tg_gate_score (N rows) -> tg_select_topk -> tg_gather_kept -> tg_gated_attention (M rows)
+`value` = prompt tokens per second = N / (wall time of one step), K steps timed
+back-to-back between two device synchronisations.  Per-stage times come from
+HIP events recorded on the launch stream inside the same timed steps.
+
+Prints ONE JSON line.  Inputs are seeded synthetic tensors of the workload's
+shape (no dataset, no trained weights): see learned_token_pruning_scorer_amd/inputs.py.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "gated-prefill input tokens/s at 16k/128k; attn TFLOP/s and select GB/s vs peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long128k")
+    ap.add_argument("--also", default="niah16k", help="second workload reported beside the main one ('' = none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-score-rows", type=int, default=8192)
+    ap.add_argument("--cpu-attn-rows", type=int, default=256)
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="if > 0: run only this many steps of the main workload, no JSON (for rocprofv3)")
+    return ap.parse_args()
+
+
+def algorithmic(w, k):
+    """Algorithmic bytes / flops of one step's stages."""
+    m = w.n_kept(k)
+    esz = 2 if w.dtype == "bf16" else 4
+    score_bytes = w.n * w.d_model * esz + w.d_hidden * w.d_model * esz + w.n * 4
+    score_flops = 2.0 * w.n * w.d_model * w.d_hidden
+    select_bytes = w.n * 4 + m * 4
+    gather_bytes = 2 * m * w.d_model * esz + m * 4 + 2 * m * 4
+    attn_flops = 4.0 * w.head_dim * w.n_q_heads * m * (m + 1) / 2
+    return dict(m=m, score_bytes=score_bytes, score_flops=score_flops, select_bytes=select_bytes,
+                gather_bytes=gather_bytes, attn_flops=attn_flops)
+
+
+class Path:
+    """Device-resident inputs and preallocated outputs of one workload."""
+
+    def __init__(self, name, binding, torch):
+        from learned_token_pruning_scorer_amd import configs, inputs
+        self.b, self.torch = binding, torch
+        self.w = w = configs.WORKLOADS[name]
+        self.k = w.budgets[0] if len(w.budgets) == 1 else w.budgets[-1]
+        self.gi = gi = inputs.gate_inputs(w)
+        dev = "cuda"
+        self.x = binding.to_device(gi.x, w.dtype, dev)
+        self.w1 = binding.to_device(gi.w1, w.dtype, dev)
+        self.w2 = binding.to_device(gi.w2, w.dtype, dev)
+        self.b1 = torch.from_numpy(gi.b1).to(dev)
+        self.m = m = w.n_kept(self.k)
+        self.scores = torch.empty(w.n, dtype=torch.float32, device=dev)
+        self.kept = torch.empty(m, dtype=torch.int32, device=dev)
+        self.ws = torch.zeros(binding.tg_select_workspace_bytes(w.n), dtype=torch.uint8, device=dev)
+        self.xk = torch.empty(m, w.d_model, dtype=self.x.dtype, device=dev)
+        self.sk = torch.empty(m, dtype=torch.float32, device=dev)
+        # Q/K/V of the kept rows (their projection from hidden states is not part of the path)
+        binding.tg_gate_score(self.x, self.w1, self.w2, self.b1, gi.b2, out=self.scores)
+        binding.tg_select_topk(self.scores, w.doc_begin, w.doc_end, self.k, out=self.kept, workspace=self.ws)
+        torch.cuda.synchronize()
+        ai = inputs.attention_inputs(w, self.kept.cpu().numpy())
+        self.q = binding.to_device(ai.q, w.dtype, dev)
+        self.kk = binding.to_device(ai.k, w.dtype, dev)
+        self.v = binding.to_device(ai.v, w.dtype, dev)
+        self.gain = torch.from_numpy(ai.gain).to(dev)
+        self.tau = ai.tau
+        self.o = torch.empty_like(self.q)
+
+    def step(self, ev=None):
+        b, w = self.b, self.w
+        if ev: ev[0].record()
+        b.tg_gate_score(self.x, self.w1, self.w2, self.b1, self.gi.b2, out=self.scores)
+        if ev: ev[1].record()
+        b.tg_select_topk(self.scores, w.doc_begin, w.doc_end, self.k, out=self.kept, workspace=self.ws)
+        if ev: ev[2].record()
+        b.tg_gather_kept(self.x, self.kept, self.scores, out=self.xk, s_out=self.sk)
+        if ev: ev[3].record()
+        b.tg_gated_attention(self.q, self.kk, self.v, self.kept, self.sk, self.gain, self.tau, out=self.o)
+        if ev: ev[4].record()
+
+    def timed(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs]) * 1e3   # us
+        return wall / steps, stage.mean(axis=0), np.median(stage, axis=0)
+
+
+def cpu_baseline(name, score_rows, attn_rows):
+    """The float64 oracle on a bounded sample of the same workload, scaled to tokens/s."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    import oracle
+    from learned_token_pruning_scorer_amd import configs, inputs
+    w = configs.WORKLOADS[name]
+    k = w.budgets[0] if len(w.budgets) == 1 else w.budgets[-1]
+    gi = inputs.gate_inputs(w)
+    g = np.random.default_rng(5)
+    rows = np.sort(g.choice(w.n, min(score_rows, w.n), replace=False))
+    x64 = inputs.to_f64(gi.x[rows], w.dtype)
+    w164, w264 = inputs.to_f64(gi.w1, w.dtype), inputs.to_f64(gi.w2, w.dtype)
+    t = time.perf_counter()
+    oracle.gate_score(x64, w164, gi.b1, w264, gi.b2)
+    t_score = (time.perf_counter() - t) * (w.n / len(rows))
+    # selection and gather run on the full workload (scores of all rows are drawn cheaply here:
+    # the oracle's own selector is timed, not the scores' provenance)
+    s_full = np.random.default_rng(6).normal(size=w.n)
+    t = time.perf_counter()
+    kept = oracle.select_topk(s_full, w.doc_begin, w.doc_end, k)
+    t_select = time.perf_counter() - t
+    t = time.perf_counter()
+    oracle.gather_kept(gi.x, s_full, kept)
+    t_gather = time.perf_counter() - t
+    ai = inputs.attention_inputs(w, kept)
+    m = len(kept)
+    arows = inputs.sample_rows(m, min(attn_rows, m), forced=(0, m - 1), seed=1)
+    q64, k64, v64 = (inputs.to_f64(a, w.dtype) for a in (ai.q, ai.k, ai.v))
+    t = time.perf_counter()
+    oracle.gated_attention(q64, k64, v64, kept, s_full[kept], ai.gain, ai.tau, rows=arows)
+    # attention cost of a row grows with the keys it sees: scale by the causal work ratio
+    work_sample = float(np.sum(arows + 1))
+    work_all = m * (m + 1) / 2.0
+    t_attn = (time.perf_counter() - t) * (work_all / work_sample)
+    total = t_score + t_select + t_gather + t_attn
+    return {"value": w.n / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{name}: gate score on {len(rows)} of {w.n} rows, full select and gather, "
+                       f"attention on {len(arows)} of {m} query rows; each scaled to the full workload "
+                       f"(score by rows, attention by causal key count)"),
+            "stage_seconds": {"score": t_score, "select": t_select, "gather": t_gather, "attention": t_attn}}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the multi-GPU design is described in DESIGN.md, not built)", file=sys.stderr)
+        return 2
+    import torch
+    from learned_token_pruning_scorer_amd import binding
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    path = Path(args.workload, binding, torch)
+    print(f"[bench] inputs ready: {args.workload}", file=sys.stderr, flush=True)
+    if args.profile_steps > 0:
+        for _ in range(args.profile_steps):
+            path.step()
+        torch.cuda.synchronize()
+        print(f"[bench] profiled {args.profile_steps} steps of {args.workload}", file=sys.stderr, flush=True)
+        return 0
+
+    sec, stage_mean, stage_med = path.timed(args.steps, args.warmup)
+    w = path.w
+    alg = algorithmic(w, path.k)
+    attn_tflops = alg["attn_flops"] / (stage_mean[3] * 1e-6) / 1e12
+    sel_gather_gbs = (alg["select_bytes"] + alg["gather_bytes"]) / ((stage_mean[1] + stage_mean[2]) * 1e-6) / 1e9
+    score_gbs = alg["score_bytes"] / (stage_mean[0] * 1e-6) / 1e9
+    score_tflops = alg["score_flops"] / (stage_mean[0] * 1e-6) / 1e12
+    print(f"[bench] {args.workload}: {sec * 1e3:.3f} ms/step; stages us (mean) score {stage_mean[0]:.1f} "
+          f"select {stage_mean[1]:.1f} gather {stage_mean[2]:.1f} attention {stage_mean[3]:.1f}",
+          file=sys.stderr, flush=True)
+
+    also = None
+    if args.also and args.also != args.workload:
+        p2 = Path(args.also, binding, torch)
+        sec2, st2, _ = p2.timed(args.steps, args.warmup)
+        also = {"workload": args.also, "tokens_per_s": p2.w.n / sec2, "ms_per_step": sec2 * 1e3,
+                "stage_us_mean": {"score": st2[0], "select": st2[1], "gather": st2[2], "attention": st2[3]}}
+        del p2
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.workload, args.cpu_score_rows, args.cpu_attn_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": w.n / sec,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, shaped like the workload; no dataset or trained weights)",
+        "config": {"workload": w.name, "n": w.n, "n_doc": w.n_doc, "k": path.k, "m": path.m,
+                   "d_model": w.d_model, "d_hidden": w.d_hidden, "n_q_heads": w.n_q_heads,
+                   "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "tau": w.tau},
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel", "achieved": attn_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "stages": {
+            "us_mean": {"score": stage_mean[0], "select": stage_mean[1], "gather": stage_mean[2],
+                        "attention": stage_mean[3]},
+            "us_median": {"score": stage_med[0], "select": stage_med[1], "gather": stage_med[2],
+                          "attention": stage_med[3]},
+            "attention_tflops": attn_tflops, "attention_frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS,
+            "select_gather_gbs": sel_gather_gbs, "select_gather_frac_hbm_peak": sel_gather_gbs / PEAK_HBM_GBS,
+            "score_gbs": score_gbs, "score_frac_hbm_peak": score_gbs / PEAK_HBM_GBS, "score_tflops": score_tflops,
+        },
+        "also": also,
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,170 @@
+/*
+ * tokengate.h -- C ABI of the TokenGate gated-prefill hot path on MI355X (gfx950).
+ *
+ * The path has four steps, one entry point each:
+ *   tg_gate_score       a small MLP scores every token's post-attention residual
+ *   tg_select_topk      keeps every question token and the K best document tokens
+ *   tg_gather_kept      compacts the kept rows (and their scores) in position order
+ *   tg_gated_attention  attention over the kept tokens with the score as a key bias
+ *
+ * Sources, cited by page title and section:
+ *   aiproducthub.cn "斯坦福伯克利TokenGate 预填充提速11.3倍", section 事件详情
+ *     (three-phase forward, MLP gate on the post-attention residual, top-K, only the
+ *     document is prunable, score as attention-logit bias with per-head gain and
+ *     temperature);
+ *   aisight.pl "TokenGate: Stanford i Berkeley ucza model, ktore tokeny pominac ...",
+ *     sections "Jak to dziala" (same mechanism) and "Wdrozenie i zastrzezenia"
+ *     (the {state} document placeholder and the max_kept_prefill_tokens budget);
+ *   news.chathome.org TokenGate article, sections
+ *     "TokenGate の学習可能なトークンプルーニングの仕組み" and
+ *     "トークンゲート付きアテンションとは".
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns every
+ *     buffer, including workspaces; the library allocates and frees nothing.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the null
+ *     stream).  The library never synchronises the stream.
+ *   - All arguments are validated on the host before anything is enqueued; on a
+ *     non-zero status nothing was enqueued and no output was touched.
+ *   - Return values are tg_status codes (int32).  TG_ERR_HIP means a launch failed
+ *     (hipGetLastError); the stream state is then undefined.
+ *   - Calls that share a workspace must not run concurrently.
+ */
+#ifndef TOKENGATE_H
+#define TOKENGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_ABI_VERSION 1
+
+/* element types of hidden states, weights, Q/K/V and outputs */
+#define TG_F32  0   /* IEEE float32 */
+#define TG_BF16 1   /* bfloat16 storage, float32 accumulation */
+
+/* status codes */
+#define TG_OK              0
+#define TG_ERR_INVALID_ARG 1   /* null pointer, negative size, bad span, bad stride ... */
+#define TG_ERR_UNSUPPORTED 2   /* a shape or alignment this build has no kernel for */
+#define TG_ERR_WORKSPACE   3   /* workspace too small */
+#define TG_ERR_HIP         4   /* the HIP runtime reported an error at launch */
+
+typedef int32_t tg_status;
+
+/* Version of this ABI (TG_ABI_VERSION of the built library). Host only. */
+int32_t tg_abi_version(void);
+
+/* Static, human-readable text for a status code. Host only; never NULL. */
+const char* tg_status_string(tg_status status);
+
+/*
+ * tg_gate_score -- the MLP gate (aiproducthub.cn, section 事件详情; aisight.pl,
+ * section "Jak to dziala").  For every row i in [0, n):
+ *
+ *     scores[i] = b2 + sum_j w2[j] * GELU( b1[j] + sum_k x[i,k] * w1[j,k] )
+ *
+ * with the exact GELU(t) = t * Phi(t) (Phi = standard normal CDF).  All n rows are
+ * scored, question tokens included, since every kept token's score later biases
+ * the attention.
+ *   dtype     TG_F32 or TG_BF16: element type of x, w1, w2
+ *   x         [n, d_model] row-major, row stride ldx elements (ldx >= d_model)
+ *   w1        [d_hidden, d_model] row-major, contiguous (output-by-input layout)
+ *   b1        [d_hidden] float32, or NULL for zero
+ *   w2        [d_hidden] in dtype
+ *   b2        (host) scalar
+ *   scores    [n] float32 output
+ * Arithmetic: bf16 operands with float32 accumulation (MFMA); GELU and the
+ * 1-wide output dot in float32.  f32: float32 throughout.
+ * Supported: n in [1, 2^31-1].  bf16: d_model % 64 == 0, d_hidden in {64, 128, 256},
+ * ldx % 8 == 0, x and w1 16-byte aligned.  f32: d_model % 4 == 0, ldx % 4 == 0,
+ * d_hidden in [1, 256].  Otherwise TG_ERR_UNSUPPORTED.
+ */
+tg_status tg_gate_score(int32_t dtype, int64_t n, int32_t d_model, int32_t d_hidden,
+                        const void* x, int64_t ldx, const void* w1, const float* b1,
+                        const void* w2, float b2, float* scores, void* stream);
+
+/*
+ * tg_num_kept -- rows above the gate (host only).  The document is the span
+ * [doc_begin, doc_end) of the prompt (the {state} placeholder, aisight.pl section
+ * "Wdrozenie i zastrzezenia"); k is the document-token budget
+ * (max_kept_prefill_tokens).  Returns (n - D) + min(k, D) with D = doc_end -
+ * doc_begin, or -1 if the arguments are invalid (n < 0, k < 0, span outside [0, n]).
+ */
+int64_t tg_num_kept(int64_t n, int64_t doc_begin, int64_t doc_end, int64_t k);
+
+/* Bytes of workspace tg_select_topk needs for n scores (host only); 0 if n < 0. */
+size_t tg_select_workspace_bytes(int64_t n);
+
+/*
+ * tg_select_topk -- document-only top-K (aiproducthub.cn, section 事件详情: only the
+ * document part of the prompt is prunable, the question never is).  Keeps every
+ * position outside [doc_begin, doc_end) and the min(k, D) document positions ranked
+ * first by (score descending, position ascending), and writes them to kept_idx in
+ * ascending position order; m = tg_num_kept(n, doc_begin, doc_end, k) entries.
+ * Ranking is exact: -0 equals +0, NaN ranks below every number (ties among NaNs
+ * again by position).  K > D keeps the whole document; K = 0 keeps none of it.
+ *   scores     [n] float32
+ *   kept_idx   [m] int32 output
+ *   workspace  >= tg_select_workspace_bytes(n) bytes, 256-byte aligned.  It must be
+ *              zero-filled before its first use; every call leaves the parts that
+ *              must start at zero (digit histograms, done counters) at zero again,
+ *              so a workspace can be reused for any n it is large enough for.
+ * Supported: n in [1, 2^31-1].
+ */
+tg_status tg_select_topk(int64_t n, const float* scores, int64_t doc_begin, int64_t doc_end,
+                         int64_t k, int32_t* kept_idx, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * tg_gather_kept -- compaction of the kept rows: layers above the gate see only the
+ * kept tokens and pruned tokens create no KV entries (aiproducthub.cn, section
+ * 事件详情; aisight.pl, section "Jak to dziala").
+ *     x_kept[r, :] = x[kept_idx[r], :],   s_kept[r] = scores[kept_idx[r]]   (r < m)
+ *   x          [n, d_model] (row stride ldx), dtype elements
+ *   kept_idx   [m] int32, entries in [0, n); a row whose index is outside [0, n) is
+ *              skipped (its output row and score are left untouched)
+ *   x_kept     [m, d_model] output, row stride ld_out >= d_model
+ *   scores, s_kept  both NULL, or both set ([n] in, [m] out, float32)
+ * A bit-exact copy.  m = 0 is a no-op.
+ */
+tg_status tg_gather_kept(int32_t dtype, int64_t n, int32_t d_model, const void* x, int64_t ldx,
+                         const int32_t* kept_idx, int64_t m, void* x_kept, int64_t ld_out,
+                         const float* scores, float* s_kept, void* stream);
+
+/*
+ * tg_gated_attention -- token-gated attention over the m kept tokens (aiproducthub.cn,
+ * section 事件详情; aisight.pl, section "Jak to dziala": each kept token's score becomes
+ * a bias on the attention logits, with a learnable per-head gain and a learnable
+ * temperature).  Adopted form, for query head h and key/value head g = h / (Hq/Hkv):
+ *
+ *     logit[i,j] = q[i,h,:].k[j,g,:] / (sqrt(head_dim) * tau) + gain[h] * s_kept[j]
+ *     out[i,h,:] = sum_{j : pos[j] <= pos[i]} softmax_j(logit[i,:]) * v[j,g,:]
+ *
+ *   q          [m, n_q_heads, head_dim], contiguous
+ *   k, v       [m, n_kv_heads, head_dim], contiguous
+ *   pos        [m] int32 original positions, strictly increasing (the output of
+ *              tg_select_topk); NULL means 0..m-1.  Key tiles wholly after a query
+ *              tile are skipped, which is exact only under this precondition.
+ *   s_kept     [m] float32 and gain [n_q_heads] float32: both set, or both NULL
+ *              (bias off)
+ *   tau        (host) temperature, finite and > 0
+ *   out        [m, n_q_heads, head_dim] in dtype (bf16 rounded to nearest even)
+ * Arithmetic (bf16): Q.K^T and P.V on bf16 MFMA with float32 accumulation, online
+ * softmax in float32 (exp2), P rounded to bf16 for the P.V product.
+ * Supported: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0; q, k, v, out
+ * 16-byte aligned.  m = 0 is a no-op.
+ */
+tg_status tg_gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                             int32_t head_dim, const void* q, const void* k, const void* v,
+                             const int32_t* pos, const float* s_kept, const float* gain, float tau,
+                             void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TOKENGATE_H */

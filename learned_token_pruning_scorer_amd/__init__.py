@@ -6,11 +6,12 @@ C-ABI library ``libtokengate.so``.  ``learned_token_pruning_scorer_amd.binding``
 holds the thin Python wrappers (same names as the C entry points); importing
 the package itself loads neither torch nor the library.
 """
+import importlib
+
 __all__ = ["configs", "inputs", "binding"]
 
 
 def __getattr__(name):
     if name == "binding":
-        from . import binding
-        return binding
+        return importlib.import_module(".binding", __name__)
     raise AttributeError(name)

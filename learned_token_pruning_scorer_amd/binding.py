@@ -1,0 +1,238 @@
+"""Thin Python binding of libtokengate.so (ctypes over torch device tensors).
+
+Functions carry the names of the C entry points.  They only marshal arguments:
+check device / dtype / contiguity, pass raw pointers and the current HIP stream,
+and turn a non-zero status into TokenGateError.  Every step of the path runs in
+the library's HIP kernels; there is no fallback.  If the library is missing the
+import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtokengate.so")
+
+TG_F32, TG_BF16 = 0, 1
+TG_OK = 0
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {text} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m learned_token_pruning_scorer_amd.build` "
+            "(the HIP library is required; there is no CPU fallback)")
+    return ctypes.CDLL(LIB_PATH)
+
+
+_lib = _load()
+_p, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_lib.tg_abi_version.restype = _i32
+_lib.tg_abi_version.argtypes = []
+_lib.tg_status_string.restype = ctypes.c_char_p
+_lib.tg_status_string.argtypes = [_i32]
+_lib.tg_gate_score.restype = _i32
+_lib.tg_gate_score.argtypes = [_i32, _i64, _i32, _i32, _p, _i64, _p, _p, _p, _f32, _p, _p]
+_lib.tg_num_kept.restype = _i64
+_lib.tg_num_kept.argtypes = [_i64, _i64, _i64, _i64]
+_lib.tg_select_workspace_bytes.restype = _sz
+_lib.tg_select_workspace_bytes.argtypes = [_i64]
+_lib.tg_select_topk.restype = _i32
+_lib.tg_select_topk.argtypes = [_i64, _p, _i64, _i64, _i64, _p, _p, _sz, _p]
+_lib.tg_gather_kept.restype = _i32
+_lib.tg_gather_kept.argtypes = [_i32, _i64, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p]
+_lib.tg_gated_attention.restype = _i32
+_lib.tg_gated_attention.argtypes = [_i32, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _f32, _p, _p]
+
+lib = _lib   # raw ctypes handle (the C ABI itself)
+
+
+def _check(fn: str, status: int):
+    if status != TG_OK:
+        raise TokenGateError(fn, status, _lib.tg_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TG_F32
+    if t.dtype == torch.bfloat16:
+        return TG_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _on_gpu(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors must be on one device")
+    return dev
+
+
+def tg_abi_version() -> int:
+    return int(_lib.tg_abi_version())
+
+
+def tg_status_string(status: int) -> str:
+    return _lib.tg_status_string(status).decode()
+
+
+def tg_num_kept(n: int, doc_begin: int, doc_end: int, k: int) -> int:
+    return int(_lib.tg_num_kept(n, doc_begin, doc_end, k))
+
+
+def tg_select_workspace_bytes(n: int) -> int:
+    return int(_lib.tg_select_workspace_bytes(n))
+
+
+def tg_gate_score(x, w1, w2, b1=None, b2: float = 0.0, out=None, stream=None):
+    """scores[i] = b2 + sum_j w2[j] GELU(b1[j] + x[i,:] . w1[j,:]) -> float32 [n]."""
+    dev = _on_gpu(x, w1, w2, b1, out)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [n, d_model] with unit column stride")
+    if w1.dtype != x.dtype or w2.dtype != x.dtype or not w1.is_contiguous() or not w2.is_contiguous():
+        raise ValueError("w1 and w2 must be contiguous and of x's dtype")
+    n, d_model = x.shape
+    d_hidden = w1.shape[0]
+    if w1.shape != (d_hidden, d_model) or w2.shape != (d_hidden,):
+        raise ValueError("shape mismatch between x, w1, w2")
+    if b1 is not None and (b1.dtype != torch.float32 or b1.shape != (d_hidden,) or not b1.is_contiguous()):
+        raise ValueError("b1 must be float32 [d_hidden]")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=dev)
+    _check("tg_gate_score", _lib.tg_gate_score(
+        _dtype_code(x), n, d_model, d_hidden, _ptr(x), x.stride(0), _ptr(w1), _ptr(b1), _ptr(w2),
+        float(b2), _ptr(out), _stream(dev, stream)))
+    return out
+
+
+_workspaces = {}
+
+
+def select_workspace(n: int, device) -> torch.Tensor:
+    """Cached, zero-filled selection workspace for `device` with room for n scores."""
+    need = tg_select_workspace_bytes(n)
+    key = torch.device(device)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 1 << 16), dtype=torch.uint8, device=key)
+        _workspaces[key] = ws
+    return ws
+
+
+def tg_select_topk(scores, doc_begin: int, doc_end: int, k: int, out=None, workspace=None, stream=None):
+    """Kept positions (int32, ascending): all non-document positions + the best min(k, D) document ones."""
+    dev = _on_gpu(scores, out, workspace)
+    if scores.dtype != torch.float32 or scores.dim() != 1 or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 vector")
+    n = scores.shape[0]
+    m = tg_num_kept(n, doc_begin, doc_end, k)
+    if m < 0:
+        raise ValueError("invalid document span or budget")
+    if out is None:
+        out = torch.empty(m, dtype=torch.int32, device=dev)
+    elif out.dtype != torch.int32 or out.numel() < m or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 tensor with room for m entries")
+    ws = workspace if workspace is not None else select_workspace(n, dev)
+    _check("tg_select_topk", _lib.tg_select_topk(
+        n, _ptr(scores), doc_begin, doc_end, k, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(dev, stream)))
+    return out[:m]
+
+
+def tg_gather_kept(x, kept_idx, scores=None, out=None, s_out=None, stream=None):
+    """(x[kept_idx], scores[kept_idx]) as new or given tensors."""
+    dev = _on_gpu(x, kept_idx, scores, out, s_out)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [n, d_model] with unit column stride")
+    if kept_idx.dtype != torch.int32 or not kept_idx.is_contiguous():
+        raise ValueError("kept_idx must be contiguous int32")
+    n, d_model = x.shape
+    m = kept_idx.shape[0]
+    if out is None:
+        out = torch.empty(m, d_model, dtype=x.dtype, device=dev)
+    elif out.dtype != x.dtype or out.shape[0] < m or out.shape[1] != d_model or out.stride(1) != 1:
+        raise ValueError("out must be [>= m, d_model] of x's dtype")
+    if scores is not None:
+        if scores.dtype != torch.float32 or not scores.is_contiguous():
+            raise ValueError("scores must be contiguous float32")
+        if s_out is None:
+            s_out = torch.empty(m, dtype=torch.float32, device=dev)
+    _check("tg_gather_kept", _lib.tg_gather_kept(
+        _dtype_code(x), n, d_model, _ptr(x), x.stride(0), _ptr(kept_idx), m, _ptr(out), out.stride(0),
+        _ptr(scores), _ptr(s_out if scores is not None else None), _stream(dev, stream)))
+    return out[:m], (s_out[:m] if scores is not None else None)
+
+
+def tg_gated_attention(q, k, v, pos=None, s_kept=None, gain=None, tau: float = 1.0, out=None, stream=None):
+    """Token-gated causal attention; q [m, Hq, d], k/v [m, Hkv, d] -> [m, Hq, d]."""
+    dev = _on_gpu(q, k, v, pos, s_kept, gain, out)
+    for t in (q, k, v):
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous [m, heads, head_dim]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    if k.shape != (m, hkv, d) or v.shape != (m, hkv, d):
+        raise ValueError("k/v shape mismatch")
+    if pos is not None and (pos.dtype != torch.int32 or pos.shape != (m,) or not pos.is_contiguous()):
+        raise ValueError("pos must be contiguous int32 [m]")
+    if (s_kept is None) != (gain is None):
+        raise ValueError("s_kept and gain must be given together")
+    if s_kept is not None:
+        if s_kept.dtype != torch.float32 or s_kept.shape != (m,) or not s_kept.is_contiguous():
+            raise ValueError("s_kept must be contiguous float32 [m]")
+        if gain.dtype != torch.float32 or gain.shape != (hq,) or not gain.is_contiguous():
+            raise ValueError("gain must be contiguous float32 [Hq]")
+    if out is None:
+        out = torch.empty_like(q)
+    _check("tg_gated_attention", _lib.tg_gated_attention(
+        _dtype_code(q), m, hq, hkv, d, _ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(s_kept), _ptr(gain),
+        float(tau), _ptr(out), _stream(dev, stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# numpy <-> torch helpers for the stored tensors of the workloads (bf16 kept as uint16 bits)
+# ---------------------------------------------------------------------------------------
+def to_device(arr, dtype: str, device="cuda"):
+    import numpy as np
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def to_host_bits(t: torch.Tensor):
+    """Device tensor -> numpy (bf16 as uint16 bit patterns, float32 as float32)."""
+    import numpy as np
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

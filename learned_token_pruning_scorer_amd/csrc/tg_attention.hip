@@ -1,0 +1,395 @@
+// Token-gated attention over the kept tokens.
+//
+// Each kept token's gate score becomes a bias on the attention logits of the
+// layers above the gate, weighted by a learnable per-head gain, and a learnable
+// temperature corrects for every query seeing fewer keys (aiproducthub.cn
+// "斯坦福伯克利TokenGate 预填充提速11.3倍", section 事件详情; aisight.pl "TokenGate:
+// Stanford i Berkeley ...", section "Jak to dziala"; news.chathome.org TokenGate
+// article, section "トークンゲート付きアテンションとは").  Adopted form:
+//     logit[i,j] = q_i . k_j / (sqrt(d) tau) + gain[h] s_kept[j],   pos[j] <= pos[i]
+//
+// bf16 kernel (flash attention for CDNA4, wave64):
+//  * a workgroup = 4 waves = 32 query rows x 4 (row-block, head) slots; the heads of
+//    one workgroup share a key/value head (grouped-query attention), so each K/V
+//    tile staged in LDS serves every wave;
+//  * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16: a
+//    lane then owns ONE query and 16 keys per 32x32 tile, so the row max / row sum
+//    are in-register plus one exchange between the two lane halves;
+//  * logits in base 2: t = (q.k) * log2(e)/(sqrt(d) tau) + log2(e) gain[h] s_kept[j]
+//    (one FMA per element; the bias row is pre-scaled once per tile in LDS);
+//  * P^T stays in registers as the B operand of O^T = V^T . P^T.  The 32x32
+//    accumulator layout leaves each lane half with keys {4h..4h+3, 8+4h..8+4h+3}
+//    of every 16-key step, so V is written to LDS transposed with the key groups of
+//    each 16-key block in the order [0, 2, 1, 3] -- one 16-byte LDS read per
+//    operand;
+//  * K/V tiles of 64 keys are double-buffered in LDS with a register prefetch of
+//    the next tile; padded LDS pitches keep the 16-byte reads conflict-free;
+//  * workgroups are numbered longest-first (the causal triangle's last query
+//    tiles first), and consecutive workgroup ids map to different key/value heads,
+//    which the dispatcher spreads round-robin over the 8 XCDs, so each XCD's L2
+//    holds the K/V of one head.
+#include "tg_common.h"
+
+namespace tg {
+
+constexpr int kAttnWaves = 4;
+constexpr int kBN = 64;   // keys per tile
+
+template <int D, int HPW>
+struct AttnCfg {
+  static constexpr int ROWS = 32 * kAttnWaves / HPW;    // query rows per workgroup
+  static constexpr int KP = D + 8;                       // K tile pitch (bf16 elements)
+  static constexpr int VP = kBN + 8;                     // V^T tile pitch
+  static constexpr int KPIECES = kBN * D / 8;            // 16-byte pieces of a K tile
+  static constexpr int K_PER_T = KPIECES / (kAttnWaves * 64);
+  static constexpr int DC = D / 8;                       // 8-wide d chunks
+  static constexpr int VGROUPS = kBN / 4;                // 4-key groups per tile
+  static_assert(KPIECES % (kAttnWaves * 64) == 0, "K pieces");
+  static_assert(VGROUPS * DC <= kAttnWaves * 64, "V staging");
+};
+
+template <int D, int HPW>
+__global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
+    int m, int hq, int hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ pos, const float* __restrict__ s_kept,
+    const float* __restrict__ gain, float c_scale, uint16_t* __restrict__ out, int n_qtiles) {
+  using C = AttnCfg<D, HPW>;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN][C::KP];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D][C::VP];
+  __shared__ __attribute__((aligned(16))) float bias_lds[2][HPW][kBN];
+  __shared__ __attribute__((aligned(16))) int32_t kpos_lds[2][kBN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+
+  // workgroup -> (key/value head, head slot, query tile), longest tiles first
+  const int group = hq / hkv;
+  const int slots_per_kv = group / HPW;
+  const int units = hkv * slots_per_kv;
+  const int unit = blockIdx.x % units;
+  const int qt = n_qtiles - 1 - blockIdx.x / units;
+  const int kvh = unit / slots_per_kv;
+  const int head0 = kvh * group + (unit % slots_per_kv) * HPW;
+  const int hh = wave % HPW;
+  const int head = head0 + hh;
+  const int q0 = qt * C::ROWS + (wave / HPW) * 32;   // this wave's first query row
+  const int row = q0 + l32;
+  const bool wave_live = q0 < m;
+  const int wave_last = min(m - 1, q0 + 31);         // last valid row of this wave
+
+  // Q fragments: B operand of S^T, lane holds Q[row][16s + 8*half .. +7]
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    if (row < m)
+      qf[s] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)row * hq + head) * D + 16 * s + 8 * half);
+    else
+      qf[s] = bf16x8{};
+  }
+  const int32_t qpos = row < m ? (pos ? pos[row] : row) : INT32_MAX;
+  const bool use_bias = s_kept != nullptr;
+  float hgain[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) hgain[j] = use_bias ? gain[head0 + j] * kLog2e : 0.f;
+
+  // ---- K/V tile staging (global -> registers -> LDS) ----
+  const int rows_end = min(m, (qt + 1) * C::ROWS);
+  const int n_tiles = (rows_end + kBN - 1) / kBN;
+  u32x4 kreg[C::K_PER_T];
+  u32x4 vreg[4];
+  float sreg = 0.f;
+  int32_t preg = INT32_MAX;
+  const int vkg = tid / C::DC, vdc = tid % C::DC;       // V staging: 4-key group, d chunk
+  const bool v_stager = vkg < C::VGROUPS;
+
+  auto load_tile = [&](int t) {
+    const int kb = t * kBN;
+#pragma unroll
+    for (int i = 0; i < C::K_PER_T; ++i) {
+      const int p = tid + i * kAttnWaves * 64;
+      const int r = p / C::DC, c = p % C::DC;
+      const int key = kb + r;
+      kreg[i] = key < m ? *reinterpret_cast<const u32x4*>(k + ((int64_t)key * hkv + kvh) * D + 8 * c)
+                        : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (v_stager) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = kb + 4 * vkg + r;
+        vreg[r] = key < m ? *reinterpret_cast<const u32x4*>(v + ((int64_t)key * hkv + kvh) * D + 8 * vdc)
+                          : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (tid < kBN) {
+      const int key = kb + tid;
+      sreg = (use_bias && key < m) ? s_kept[key] : 0.f;
+      preg = key < m ? (pos ? pos[key] : key) : INT32_MAX;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < C::K_PER_T; ++i) {
+      const int p = tid + i * kAttnWaves * 64;
+      const int r = p / C::DC, c = p % C::DC;
+      *reinterpret_cast<u32x4*>(&k_lds[buf][r][8 * c]) = kreg[i];
+    }
+    if (v_stager) {
+      // 4 keys x 8 d -> 8 rows of V^T, 4 keys (8 bytes) each, key groups of every
+      // 16-key block stored in the order [0, 2, 1, 3]
+      const int g4 = vkg & 3;
+      const int col = (vkg >> 2) * 16 + ((g4 == 1) ? 8 : (g4 == 2) ? 4 : (g4 == 3 ? 12 : 0));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1, sh = (e & 1) * 16;
+        const uint32_t a0 = (vreg[0][w] >> sh) & 0xffffu, a1 = (vreg[1][w] >> sh) & 0xffffu;
+        const uint32_t a2 = (vreg[2][w] >> sh) & 0xffffu, a3 = (vreg[3][w] >> sh) & 0xffffu;
+        u32x2 pk = {a0 | (a1 << 16), a2 | (a3 << 16)};
+        *reinterpret_cast<u32x2*>(&vt_lds[buf][8 * vdc + e][col]) = pk;
+      }
+    }
+    if (tid < kBN) {
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) bias_lds[buf][j][tid] = sreg * hgain[j];
+      kpos_lds[buf][tid] = preg;
+    }
+  };
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[u][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const int kb = t * kBN;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+
+    if (wave_live && kb <= wave_last) {
+      // S^T tile: keys kb + 32*kt + (8*(i/4) + 4*half + i%4), query = row
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][32 * kt + l32][16 * s + 8 * half]);
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
+        }
+      }
+      const bool need_mask = (kb + kBN - 1 > q0) || (kb + kBN > m);
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int kk = 32 * kt + 8 * g + 4 * half;
+          const f32x4 bb = *reinterpret_cast<const f32x4*>(&bias_lds[buf][hh][kk]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = fmaf(sacc[kt][4 * g + r], c_scale, bb[r]);
+            if (need_mask && kpos_lds[buf][kk + r] > qpos) x = -INFINITY;
+            sacc[kt][4 * g + r] = x;
+            mt = fmaxf(mt, x);
+          }
+        }
+      mt = fmaxf(mt, swap_halves(mt));
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(sacc[kt][i] - m_new);
+          sacc[kt][i] = p;
+          lsum += p;
+        }
+      l_run = fmaf(l_run, alpha, lsum);
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[u][i] *= alpha;
+      // P^T fragments: step s2 covers keys 16*s2 .. +15; element e of lane half h is
+      // key 16*s2 + (e < 4 ? 4h + e : 8 + 4h + e - 4) = registers 8*(s2%2) + e of tile s2/2
+      bf16x8 pf[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        u32x4_t w;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+          w[e2] = pack_bf16x2(sacc[s2 >> 1][8 * (s2 & 1) + 2 * e2], sacc[s2 >> 1][8 * (s2 & 1) + 2 * e2 + 1]);
+        pf[s2] = __builtin_bit_cast(bf16x8, w);
+      }
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt_lds[buf][32 * u + l32][16 * s2 + 8 * half]);
+          oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s2], oacc[u], 0, 0, 0);
+        }
+    }
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + swap_halves(l_run);   // wave-uniform exchange
+  if (row < m) {
+    const float inv = 1.0f / l_tot;
+    uint16_t* orow = out + ((int64_t)row * hq + head) * D;
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * u + 8 * g + 4 * half;
+        u32x2 pk = {pack_bf16x2(oacc[u][4 * g] * inv, oacc[u][4 * g + 1] * inv),
+                    pack_bf16x2(oacc[u][4 * g + 2] * inv, oacc[u][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + d0) = pk;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// float32 path: one thread per (query row, head); K/V tiles of 32 keys in LDS.
+// ---------------------------------------------------------------------------------
+constexpr int kF32Rows = 64;
+constexpr int kF32Keys = 32;
+
+template <int D>
+__global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(int m, int hq, int hkv, const float* __restrict__ q,
+                                                            const float* __restrict__ k,
+                                                            const float* __restrict__ v,
+                                                            const int32_t* __restrict__ pos,
+                                                            const float* __restrict__ s_kept,
+                                                            const float* __restrict__ gain, float c_scale,
+                                                            float* __restrict__ out) {
+  __shared__ float ks[kF32Keys][D];
+  __shared__ float vs[kF32Keys][D];
+  __shared__ float bs[kF32Keys];
+  __shared__ int32_t ps[kF32Keys];
+  const int head = blockIdx.y;
+  const int kvh = head / (hq / hkv);
+  const int row = blockIdx.x * kF32Rows + threadIdx.x;
+  const bool live = row < m;
+  float qv[D], ov[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    qv[c] = live ? q[((int64_t)row * hq + head) * D + c] : 0.f;
+    ov[c] = 0.f;
+  }
+  const int32_t qpos = live ? (pos ? pos[row] : row) : INT32_MAX;
+  const float hg = s_kept ? gain[head] * kLog2e : 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const int rows_end = min(m, (int)(blockIdx.x + 1) * kF32Rows);
+  for (int kb = 0; kb < rows_end; kb += kF32Keys) {
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kF32Keys * D; idx += kF32Rows) {
+      const int r = idx / D, c = idx % D;
+      const int key = kb + r;
+      ks[r][c] = key < m ? k[((int64_t)key * hkv + kvh) * D + c] : 0.f;
+      vs[r][c] = key < m ? v[((int64_t)key * hkv + kvh) * D + c] : 0.f;
+    }
+    if (threadIdx.x < kF32Keys) {
+      const int key = kb + threadIdx.x;
+      bs[threadIdx.x] = (s_kept && key < m) ? s_kept[key] * hg : 0.f;
+      ps[threadIdx.x] = key < m ? (pos ? pos[key] : key) : INT32_MAX;
+    }
+    __syncthreads();
+    if (!live) continue;
+    for (int r = 0; r < kF32Keys; ++r) {
+      if (ps[r] > qpos) continue;
+      float dot = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) dot = fmaf(qv[c], ks[r][c], dot);
+      const float t = fmaf(dot, c_scale, bs[r]);
+      const float m_new = fmaxf(m_run, t);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      const float p = __builtin_amdgcn_exp2f(t - m_new);
+      l_run = fmaf(l_run, alpha, p);
+#pragma unroll
+      for (int c = 0; c < D; ++c) ov[c] = fmaf(ov[c], alpha, p * vs[r][c]);
+      m_run = m_new;
+    }
+  }
+  if (live) {
+    const float inv = 1.0f / l_run;
+#pragma unroll
+    for (int c = 0; c < D; ++c) out[((int64_t)row * hq + head) * D + c] = ov[c] * inv;
+  }
+}
+
+template <int D, int HPW>
+static tg_status launch_attn_bf16(int m, int hq, int hkv, const void* q, const void* k, const void* v,
+                                  const int32_t* pos, const float* s_kept, const float* gain, float c_scale,
+                                  void* out, hipStream_t st) {
+  using C = AttnCfg<D, HPW>;
+  const int n_qtiles = (m + C::ROWS - 1) / C::ROWS;
+  const int64_t grid = (int64_t)n_qtiles * (hq / HPW);
+  if (grid > INT32_MAX) return TG_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((attn_bf16_kernel<D, HPW>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0, st, m, hq, hkv,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, static_cast<uint16_t*>(out),
+                     n_qtiles);
+  TG_CHECK_LAUNCH();
+  return TG_OK;
+}
+
+template <int D>
+static tg_status dispatch_attn_bf16(int m, int hq, int hkv, const void* q, const void* k, const void* v,
+                                    const int32_t* pos, const float* s_kept, const float* gain, float c_scale,
+                                    void* out, hipStream_t st) {
+  const int group = hq / hkv;
+  if (group % 4 == 0) return launch_attn_bf16<D, 4>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, out, st);
+  if (group % 2 == 0) return launch_attn_bf16<D, 2>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, out, st);
+  return launch_attn_bf16<D, 1>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, out, st);
+}
+
+}  // namespace tg
+
+extern "C" tg_status tg_gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t head_dim, const void* q, const void* k, const void* v,
+                                        const int32_t* pos, const float* s_kept, const float* gain, float tau,
+                                        void* out, void* stream) {
+  using namespace tg;
+  if (dtype != TG_F32 && dtype != TG_BF16) return TG_ERR_INVALID_ARG;
+  if (m < 0 || m > INT32_MAX || n_q_heads <= 0 || n_kv_heads <= 0) return TG_ERR_INVALID_ARG;
+  if (n_q_heads % n_kv_heads != 0) return TG_ERR_INVALID_ARG;
+  if ((s_kept == nullptr) != (gain == nullptr)) return TG_ERR_INVALID_ARG;
+  if (!std::isfinite(tau) || !(tau > 0.f)) return TG_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return TG_ERR_UNSUPPORTED;
+  if (m == 0) return TG_OK;
+  if (!q || !k || !v || !out) return TG_ERR_INVALID_ARG;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                          reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
+  if (align & 15u) return TG_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float c_scale = static_cast<float>(1.4426950408889634 / (std::sqrt((double)head_dim) * (double)tau));
+  const int mm = static_cast<int>(m);
+  if (dtype == TG_BF16) {
+    return head_dim == 128
+               ? dispatch_attn_bf16<128>(mm, n_q_heads, n_kv_heads, q, k, v, pos, s_kept, gain, c_scale, out, st)
+               : dispatch_attn_bf16<64>(mm, n_q_heads, n_kv_heads, q, k, v, pos, s_kept, gain, c_scale, out, st);
+  }
+  const dim3 grid((mm + kF32Rows - 1) / kF32Rows, n_q_heads);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(kF32Rows), 0, st, mm, n_q_heads, n_kv_heads,
+                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                       pos, s_kept, gain, c_scale, static_cast<float*>(out));
+  else
+    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(kF32Rows), 0, st, mm, n_q_heads, n_kv_heads,
+                       static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+                       pos, s_kept, gain, c_scale, static_cast<float*>(out));
+  TG_CHECK_LAUNCH();
+  return TG_OK;
+}

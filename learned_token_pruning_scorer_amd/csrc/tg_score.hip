@@ -1,0 +1,286 @@
+// Gate scorer: s[i] = b2 + sum_j w2[j] * GELU(b1[j] + x[i,:] . w1[j,:]).
+//
+// The MLP gate of TokenGate (aiproducthub.cn "斯坦福伯克利TokenGate 预填充提速11.3倍",
+// section 事件详情; aisight.pl "TokenGate: Stanford i Berkeley ...", section
+// "Jak to dziala") scores each token's post-attention residual with a small MLP.
+//
+// bf16 path: one workgroup of 8 waves owns BT tokens and ALL d_hidden units, so
+// the GELU and the 1-wide w2 dot finish inside the workgroup (no partial hidden
+// activations ever reach memory).  The product is computed transposed,
+// C^T[hidden, token] = W1 . X^T, on v_mfma_f32_32x32x16_bf16: each lane of a
+// 32x32 accumulator then holds one token and 16 hidden units, so the epilogue
+// reduction over hidden units is mostly in-register.  Both operands are staged
+// through LDS in k-chunks of 64 (double-buffered); X streams from HBM once and
+// W1 (<= 1 MiB) is re-read from L2 by every workgroup.
+#include "tg_common.h"
+
+namespace tg {
+
+// GELU(h) = h * Phi(h), Phi the standard normal CDF.  Phi comes from the rational
+// approximation of erfc in Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (|error| <= 1.5e-7 on erfc): for a = |h|/sqrt(2) >= 0,
+//   erfc(a) ~= (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-a^2),  t = 1/(1 + p a),
+// and Phi(h) = 1 - erfc(a)/2 for h >= 0, erfc(a)/2 for h < 0.  In float32 the GELU
+// error stays below 4e-7 absolute.  This costs ~12 VALU ops and two transcendentals
+// (rcp, exp2) per value and keeps few registers live.
+__device__ __forceinline__ float gelu_exact(float h) {
+  constexpr float p_over_sqrt2 = 0.3275911f * 0.70710678118654752f;
+  constexpr float a1 = 0.5f * 0.254829592f, a2 = 0.5f * -0.284496736f, a3 = 0.5f * 1.421413741f,
+                  a4 = 0.5f * -1.453152027f, a5 = 0.5f * 1.061405429f;   // halved: q = erfc/2
+  const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(h), p_over_sqrt2, 1.0f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, a5, a4), a3), a2), a1);
+  const float q = poly * __builtin_amdgcn_exp2f(h * h * (-0.5f * kLog2e));   // = erfc(|h|/sqrt2)/2
+  const float hq = h * q;
+  return h >= 0.0f ? h - hq : hq;
+}
+
+// ---------------------------------------------------------------------------------
+// float32 path (small shapes): thread j of the block owns hidden unit j.
+// ---------------------------------------------------------------------------------
+constexpr int kF32Toks = 8;
+constexpr int kF32KC = 256;
+
+__global__ __launch_bounds__(256) void score_f32_kernel(int n, int d_model, int d_hidden,
+                                                        const float* __restrict__ x, int64_t ldx,
+                                                        const float* __restrict__ w1,
+                                                        const float* __restrict__ b1,
+                                                        const float* __restrict__ w2, float b2,
+                                                        float* __restrict__ scores) {
+  __shared__ float xs[kF32Toks][kF32KC];
+  __shared__ float red[kF32Toks][4];
+  const int t0 = blockIdx.x * kF32Toks;
+  const int j = threadIdx.x;
+  float acc[kF32Toks];
+#pragma unroll
+  for (int r = 0; r < kF32Toks; ++r) acc[r] = 0.f;
+
+  for (int k0 = 0; k0 < d_model; k0 += kF32KC) {
+    const int kc = min(kF32KC, d_model - k0);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kF32Toks * kF32KC; idx += 256) {
+      const int r = idx / kF32KC, c = idx % kF32KC;
+      xs[r][c] = (t0 + r < n && c < kc) ? x[(int64_t)(t0 + r) * ldx + k0 + c] : 0.f;
+    }
+    __syncthreads();
+    if (j < d_hidden) {
+      const float* wr = w1 + (int64_t)j * d_model + k0;
+      for (int c = 0; c < kc; ++c) {
+        const float w = wr[c];
+#pragma unroll
+        for (int r = 0; r < kF32Toks; ++r) acc[r] = fmaf(xs[r][c], w, acc[r]);
+      }
+    }
+  }
+  const float bb = (j < d_hidden && b1) ? b1[j] : 0.f;
+  const float ww = (j < d_hidden) ? w2[j] : 0.f;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int r = 0; r < kF32Toks; ++r) {
+    float v = (j < d_hidden) ? ww * gelu_exact(acc[r] + bb) : 0.f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) red[r][wave] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < kF32Toks && t0 + threadIdx.x < n) {
+    const int r = threadIdx.x;
+    scores[t0 + r] = b2 + ((red[r][0] + red[r][1]) + (red[r][2] + red[r][3]));
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// bf16 path
+// ---------------------------------------------------------------------------------
+constexpr int kScoreWaves = 8;
+constexpr int kScoreKC = 64;              // k-chunk staged per step
+constexpr int kScorePitch = kScoreKC + 8; // LDS row pitch in bf16 (144 B: conflict-free b128 reads)
+
+template <int H, int BTW>
+struct ScoreTile {
+  static constexpr int HT = H / 32;               // 32-row hidden tiles in total
+  static constexpr int AT = HT < 4 ? HT : 4;      // hidden tiles per wave
+  static constexpr int WH = HT / AT;              // waves along hidden
+  static constexpr int WT = kScoreWaves / WH;     // waves along tokens
+  static constexpr int BT = 32 * BTW * WT;        // tokens per workgroup
+  static constexpr int W_PIECES = H * (kScoreKC / 8);   // 16-byte pieces of a W1 chunk
+  static constexpr int X_PIECES = BT * (kScoreKC / 8);
+  static constexpr int W_PER_T = W_PIECES / (kScoreWaves * 64);
+  static constexpr int X_PER_T = X_PIECES / (kScoreWaves * 64);
+  static_assert(HT % AT == 0 && kScoreWaves % WH == 0, "tile shape");
+  static_assert(W_PIECES % (kScoreWaves * 64) == 0 && X_PIECES % (kScoreWaves * 64) == 0, "pieces");
+};
+
+template <int H, int BTW>
+__global__ __launch_bounds__(kScoreWaves * 64) void score_bf16_kernel(
+    int n, int d_model, const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w1,
+    const float* __restrict__ b1, const uint16_t* __restrict__ w2, float b2, float* __restrict__ scores) {
+  using T = ScoreTile<H, BTW>;
+  constexpr int BT = T::BT, AT = T::AT, WT = T::WT;
+  __shared__ __attribute__((aligned(16))) uint16_t lw[2][H][kScorePitch];
+  __shared__ __attribute__((aligned(16))) uint16_t lx[2][BT][kScorePitch];
+  __shared__ __attribute__((aligned(16))) float w2f[H];
+  __shared__ __attribute__((aligned(16))) float b1f[H];
+  __shared__ float red[T::WH][BT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int wh = wave / WT, wt = wave % WT;
+  const int tok0 = blockIdx.x * BT;
+
+  for (int i = tid; i < H; i += kScoreWaves * 64) {
+    w2f[i] = bf16_to_f32(w2[i]);
+    b1f[i] = b1 ? b1[i] : 0.f;
+  }
+
+  // global -> register staging of one k-chunk
+  u32x4 wreg[T::W_PER_T], xreg[T::X_PER_T];
+  auto load_chunk = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < T::W_PER_T; ++i) {
+      const int p = tid + i * kScoreWaves * 64;
+      const int row = p / (kScoreKC / 8), c = p % (kScoreKC / 8);
+      wreg[i] = *reinterpret_cast<const u32x4*>(w1 + (int64_t)row * d_model + k0 + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < T::X_PER_T; ++i) {
+      const int p = tid + i * kScoreWaves * 64;
+      const int row = p / (kScoreKC / 8), c = p % (kScoreKC / 8);
+      const int tok = tok0 + row;
+      xreg[i] = (tok < n) ? *reinterpret_cast<const u32x4*>(x + (int64_t)tok * ldx + k0 + c * 8)
+                          : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < T::W_PER_T; ++i) {
+      const int p = tid + i * kScoreWaves * 64;
+      const int row = p / (kScoreKC / 8), c = p % (kScoreKC / 8);
+      *reinterpret_cast<u32x4*>(&lw[buf][row][c * 8]) = wreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < T::X_PER_T; ++i) {
+      const int p = tid + i * kScoreWaves * 64;
+      const int row = p / (kScoreKC / 8), c = p % (kScoreKC / 8);
+      *reinterpret_cast<u32x4*>(&lx[buf][row][c * 8]) = xreg[i];
+    }
+  };
+
+  f32x16 acc[AT][BTW];
+#pragma unroll
+  for (int a = 0; a < AT; ++a)
+#pragma unroll
+    for (int b = 0; b < BTW; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  const int nchunks = d_model / kScoreKC;
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int buf = ch & 1;
+    if (ch + 1 < nchunks) load_chunk((ch + 1) * kScoreKC);
+#pragma unroll
+    for (int ks = 0; ks < kScoreKC / 16; ++ks) {
+      bf16x8 af[AT], bfr[BTW];
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+        af[a] = *reinterpret_cast<const bf16x8*>(&lw[buf][32 * (wh * AT + a) + l32][16 * ks + 8 * half]);
+#pragma unroll
+      for (int b = 0; b < BTW; ++b)
+        bfr[b] = *reinterpret_cast<const bf16x8*>(&lx[buf][32 * (wt * BTW + b) + l32][16 * ks + 8 * half]);
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+#pragma unroll
+        for (int b = 0; b < BTW; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+    }
+    if (ch + 1 < nchunks) store_chunk(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds token (32*(wt*BTW+b) + l32) and hidden units
+  // 32*(wh*AT+a) + 8*g + 4*half + r  (g = 0..3, r = 0..3) of tile (a, b)
+  float part[BTW];
+#pragma unroll
+  for (int b = 0; b < BTW; ++b) part[b] = 0.f;
+#pragma unroll
+  for (int a = 0; a < AT; ++a)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int hid = 32 * (wh * AT + a) + 8 * g + 4 * half;
+      const f32x4 ww = *reinterpret_cast<const f32x4*>(&w2f[hid]);
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(&b1f[hid]);
+#pragma unroll
+      for (int b = 0; b < BTW; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[b] = fmaf(ww[r], gelu_exact(acc[a][b][4 * g + r] + bb[r]), part[b]);
+    }
+#pragma unroll
+  for (int b = 0; b < BTW; ++b) {
+    part[b] += swap_halves(part[b]);
+    if (half == 0) red[wh][32 * (wt * BTW + b) + l32] = part[b];
+  }
+  __syncthreads();
+  for (int t = tid; t < BT; t += kScoreWaves * 64) {
+    if (tok0 + t < n) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < T::WH; ++w) s += red[w][t];
+      scores[tok0 + t] = s + b2;
+    }
+  }
+}
+
+template <int H, int BTW>
+static tg_status launch_score_bf16(int n, int d_model, const void* x, int64_t ldx, const void* w1,
+                                   const float* b1, const void* w2, float b2, float* scores,
+                                   hipStream_t stream) {
+  constexpr int BT = ScoreTile<H, BTW>::BT;
+  const int grid = (n + BT - 1) / BT;
+  hipLaunchKernelGGL((score_bf16_kernel<H, BTW>), dim3(grid), dim3(kScoreWaves * 64), 0, stream, n,
+                     d_model, static_cast<const uint16_t*>(x), ldx, static_cast<const uint16_t*>(w1),
+                     b1, static_cast<const uint16_t*>(w2), b2, scores);
+  TG_CHECK_LAUNCH();
+  return TG_OK;
+}
+
+}  // namespace tg
+
+extern "C" tg_status tg_gate_score(int32_t dtype, int64_t n, int32_t d_model, int32_t d_hidden,
+                                   const void* x, int64_t ldx, const void* w1, const float* b1,
+                                   const void* w2, float b2, float* scores, void* stream) {
+  using namespace tg;
+  if (dtype != TG_F32 && dtype != TG_BF16) return TG_ERR_INVALID_ARG;
+  if (!x || !w1 || !w2 || !scores) return TG_ERR_INVALID_ARG;
+  if (n <= 0 || n > INT32_MAX || d_model <= 0 || d_hidden <= 0 || ldx < d_model) return TG_ERR_INVALID_ARG;
+  if (!std::isfinite(b2)) return TG_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == TG_F32) {
+    if (d_hidden > 256) return TG_ERR_UNSUPPORTED;
+    const int grid = static_cast<int>((n + kF32Toks - 1) / kF32Toks);
+    hipLaunchKernelGGL(score_f32_kernel, dim3(grid), dim3(256), 0, st, static_cast<int>(n), d_model,
+                       d_hidden, static_cast<const float*>(x), ldx, static_cast<const float*>(w1), b1,
+                       static_cast<const float*>(w2), b2, scores);
+    TG_CHECK_LAUNCH();
+    return TG_OK;
+  }
+  if (d_model % kScoreKC != 0 || ldx % 8 != 0) return TG_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w1)) & 15u) return TG_ERR_UNSUPPORTED;
+  const int nn = static_cast<int>(n);
+  // d_hidden 256: 256-token tiles once there are enough of them to fill the chip (halves the
+  // L2 re-reads of W1 per token); 64/128 always use 256-token tiles (8 waves along tokens).
+  const bool big = n >= 65536;
+  switch (d_hidden) {
+    case 64:
+      return launch_score_bf16<64, 1>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
+    case 128:
+      return launch_score_bf16<128, 1>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
+    case 256:
+      return big ? launch_score_bf16<256, 2>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st)
+                 : launch_score_bf16<256, 1>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
+    default:
+      return TG_ERR_UNSUPPORTED;
+  }
+}

@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every declared symbol, and its host-side
+logic (sizes, status text, argument validation) behaves as documented.
+
+No case here launches a kernel: every call either is host-only or fails
+validation before anything is enqueued, so these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tokengate.h")
+LIB = os.path.join(ROOT, "learned_token_pruning_scorer_amd", "libtokengate.so")
+
+TG_OK, TG_ERR_INVALID_ARG, TG_ERR_UNSUPPORTED, TG_ERR_WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(1 << 20)     # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libtokengate.so is not built (python -m learned_token_pruning_scorer_amd.build)")
+    lib = ctypes.CDLL(LIB)
+    i32, i64, p, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
+    lib.tg_status_string.restype = ctypes.c_char_p
+    lib.tg_status_string.argtypes = [i32]
+    lib.tg_num_kept.restype = i64
+    lib.tg_num_kept.argtypes = [i64] * 4
+    lib.tg_select_workspace_bytes.restype = sz
+    lib.tg_select_workspace_bytes.argtypes = [i64]
+    lib.tg_gate_score.argtypes = [i32, i64, i32, i32, p, i64, p, p, p, f32, p, p]
+    lib.tg_select_topk.argtypes = [i64, p, i64, i64, i64, p, p, sz, p]
+    lib.tg_gather_kept.argtypes = [i32, i64, i32, p, i64, p, i64, p, i64, p, p, p]
+    lib.tg_gated_attention.argtypes = [i32, i64, i32, i32, i32, p, p, p, p, p, p, f32, p, p]
+    return lib
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"tg_gate_score", "tg_select_topk", "tg_gather_kept", "tg_gated_attention"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in tokengate.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.tg_abi_version() == 1
+    for code in range(5):
+        assert lib.tg_status_string(code).startswith(b"TG_")
+    assert lib.tg_status_string(99) == b"unknown tg_status"
+
+
+def test_num_kept(lib):
+    assert lib.tg_num_kept(512, 0, 448, 128) == 192
+    assert lib.tg_num_kept(131072, 0, 131008, 8192) == 8256
+    assert lib.tg_num_kept(100, 10, 20, 500) == 100          # K > D keeps the whole document
+    assert lib.tg_num_kept(100, 10, 20, 0) == 90             # K = 0 keeps only the rest
+    assert lib.tg_num_kept(100, 50, 50, 7) == 100            # empty document
+    assert lib.tg_num_kept(100, 20, 10, 1) == -1
+    assert lib.tg_num_kept(100, 0, 101, 1) == -1
+    assert lib.tg_num_kept(100, 0, 10, -1) == -1
+
+
+def test_workspace_size_grows_with_n(lib):
+    a, b = lib.tg_select_workspace_bytes(1), lib.tg_select_workspace_bytes(1 << 20)
+    assert a > 0 and b > a and a % 256 == 0 and b % 256 == 0
+    assert lib.tg_select_workspace_bytes(-1) == 0
+
+
+def test_gate_score_validation(lib):
+    # null pointers, bad sizes, bad dtype, unsupported shapes
+    assert lib.tg_gate_score(1, 16, 64, 64, None, 64, FAKE, None, FAKE, 0.0, FAKE, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_gate_score(1, 0, 64, 64, FAKE, 64, FAKE, None, FAKE, 0.0, FAKE, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_gate_score(1, 16, 64, 64, FAKE, 32, FAKE, None, FAKE, 0.0, FAKE, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_gate_score(7, 16, 64, 64, FAKE, 64, FAKE, None, FAKE, 0.0, FAKE, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_gate_score(1, 16, 64, 64, FAKE, 64, FAKE, None, FAKE, float("nan"), FAKE, None) \
+        == TG_ERR_INVALID_ARG
+    assert lib.tg_gate_score(1, 16, 96, 64, FAKE, 96, FAKE, None, FAKE, 0.0, FAKE, None) == TG_ERR_UNSUPPORTED
+    assert lib.tg_gate_score(1, 16, 64, 96, FAKE, 64, FAKE, None, FAKE, 0.0, FAKE, None) == TG_ERR_UNSUPPORTED
+    assert lib.tg_gate_score(1, 16, 64, 64, FAKE, 68, FAKE, None, FAKE, 0.0, FAKE, None) == TG_ERR_UNSUPPORTED
+    assert lib.tg_gate_score(0, 16, 64, 300, FAKE, 64, FAKE, None, FAKE, 0.0, FAKE, None) == TG_ERR_UNSUPPORTED
+
+
+def test_select_validation(lib):
+    ws = ctypes.c_void_p(1 << 20)
+    need = lib.tg_select_workspace_bytes(1000)
+    assert lib.tg_select_topk(1000, None, 0, 900, 10, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk(1000, FAKE, 0, 900, 10, None, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk(1000, FAKE, 901, 900, 10, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk(1000, FAKE, 0, 1001, 10, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk(1000, FAKE, 0, 900, -1, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk(0, FAKE, 0, 0, 1, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk(1000, FAKE, 0, 900, 10, FAKE, ctypes.c_void_p((1 << 20) + 4), need, None) \
+        == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk(1000, FAKE, 0, 900, 10, FAKE, ws, need - 1, None) == TG_ERR_WORKSPACE
+
+
+def test_gather_validation(lib):
+    assert lib.tg_gather_kept(1, 100, 64, FAKE, 32, FAKE, 10, FAKE, 64, None, None, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_gather_kept(1, 100, 64, FAKE, 64, FAKE, 10, FAKE, 32, None, None, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_gather_kept(1, 100, 64, FAKE, 64, FAKE, 10, FAKE, 64, FAKE, None, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_gather_kept(1, 100, 64, None, 64, FAKE, 10, FAKE, 64, None, None, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_gather_kept(1, 100, 64, FAKE, 64, FAKE, -1, FAKE, 64, None, None, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_gather_kept(3, 100, 64, FAKE, 64, FAKE, 10, FAKE, 64, None, None, None) == TG_ERR_INVALID_ARG
+    # m = 0 is a no-op that succeeds without touching anything
+    assert lib.tg_gather_kept(1, 100, 64, FAKE, 64, FAKE, 0, FAKE, 64, None, None, None) == TG_OK
+
+
+def test_attention_validation(lib):
+    f = ctypes.c_float
+    args = lambda **kw: [kw.get("dt", 1), kw.get("m", 64), kw.get("hq", 4), kw.get("hkv", 2), kw.get("d", 64),
+                         kw.get("q", FAKE), FAKE, FAKE, None, kw.get("s", None), kw.get("g", None),
+                         f(kw.get("tau", 1.0)), FAKE, None]
+    assert lib.tg_gated_attention(*args(hq=3, hkv=2)) == TG_ERR_INVALID_ARG
+    assert lib.tg_gated_attention(*args(tau=0.0)) == TG_ERR_INVALID_ARG
+    assert lib.tg_gated_attention(*args(tau=float("inf"))) == TG_ERR_INVALID_ARG
+    assert lib.tg_gated_attention(*args(s=FAKE)) == TG_ERR_INVALID_ARG
+    assert lib.tg_gated_attention(*args(m=-1)) == TG_ERR_INVALID_ARG
+    assert lib.tg_gated_attention(*args(q=None)) == TG_ERR_INVALID_ARG
+    assert lib.tg_gated_attention(*args(d=96)) == TG_ERR_UNSUPPORTED
+    assert lib.tg_gated_attention(*args(q=ctypes.c_void_p((1 << 20) + 2))) == TG_ERR_UNSUPPORTED
+    assert lib.tg_gated_attention(*args(m=0)) == TG_OK
