@@ -113,6 +113,7 @@ size_t tg_select_workspace_bytes(int64_t n);
  *              zero-filled before its first use; every call leaves the parts that
  *              must start at zero (digit histograms, done counters) at zero again,
  *              so a workspace can be reused for any n it is large enough for.
+ * m = 0 (the whole prompt is a document and k = 0) is a no-op.
  * Supported: n in [1, 2^31-1].
  */
 tg_status tg_select_topk(int64_t n, const float* scores, int64_t doc_begin, int64_t doc_end,

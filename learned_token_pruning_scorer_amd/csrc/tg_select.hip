@@ -249,8 +249,9 @@ extern "C" tg_status tg_select_topk(int64_t n, const float* scores, int64_t doc_
                                     int64_t k, int32_t* kept_idx, void* workspace, size_t workspace_bytes,
                                     void* stream) {
   using namespace tg;
-  if (!scores || !kept_idx || !workspace) return TG_ERR_INVALID_ARG;
   if (n <= 0 || n > INT32_MAX || tg_num_kept(n, doc_begin, doc_end, k) < 0) return TG_ERR_INVALID_ARG;
+  if (tg_num_kept(n, doc_begin, doc_end, k) == 0) return TG_OK;   // nothing kept, nothing to write
+  if (!scores || !kept_idx || !workspace) return TG_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return TG_ERR_INVALID_ARG;
   const SelLayout L;
   if (workspace_bytes < L.bytes(n)) return TG_ERR_WORKSPACE;

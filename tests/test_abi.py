@@ -100,6 +100,8 @@ def test_select_validation(lib):
     assert lib.tg_select_topk(1000, FAKE, 0, 900, 10, FAKE, ctypes.c_void_p((1 << 20) + 4), need, None) \
         == TG_ERR_INVALID_ARG
     assert lib.tg_select_topk(1000, FAKE, 0, 900, 10, FAKE, ws, need - 1, None) == TG_ERR_WORKSPACE
+    # nothing kept (all document, k = 0): a no-op that succeeds without any pointer
+    assert lib.tg_select_topk(1000, None, 0, 1000, 0, None, None, 0, None) == TG_OK
 
 
 def test_gather_validation(lib):
