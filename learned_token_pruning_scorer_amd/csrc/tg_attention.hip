@@ -15,13 +15,20 @@
 //  * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16: a
 //    lane then owns ONE query and 16 keys per 32x32 tile, so the row max / row sum
 //    are in-register plus one exchange between the two lane halves;
-//  * logits in base 2: t = (q.k) * log2(e)/(sqrt(d) tau) + log2(e) gain[h] s_kept[j]
-//    (one FMA per element; the bias row is pre-scaled once per tile in LDS);
-//  * P^T stays in registers as the B operand of O^T = V^T . P^T.  The 32x32
+//  * the key bias enters through the MFMA accumulator: S^T starts from
+//    gain[h] s_kept[j] sqrt(d) tau (the bias in q.k units, staged per tile in LDS),
+//    so S = q.k + that and the base-2 logit is S * log2(e)/(sqrt(d) tau) -- one FMA
+//    with the running max folded in gives the exponent;
+//  * lazy rescaling: the running max (and with it O and the row sum) is only moved
+//    when a tile's max exceeds it by more than 8 in the base-2 exponent, so P stays
+//    below 2^8 and most tiles skip the O rescale;
+//  * P^T stays in registers as the B operand of O^T = V^T . P^T; its row sums come
+//    from v_dot2_f32_bf16 on the packed bf16 P that the MFMA consumes.  The 32x32
 //    accumulator layout leaves each lane half with keys {4h..4h+3, 8+4h..8+4h+3}
-//    of every 16-key step, so V is written to LDS transposed with the key groups of
-//    each 16-key block in the order [0, 2, 1, 3] -- one 16-byte LDS read per
-//    operand;
+//    of every 16-key step, so V is written to LDS transposed (v_perm_b32 packs)
+//    with the key groups of each 16-key block in the order [0, 2, 1, 3] and the
+//    16-byte chunks of each 128-byte V^T row XOR-swizzled by (row/2) mod 8, which
+//    makes both the transposed writes and the operand reads bank-conflict free;
 //  * K/V tiles of 64 keys are double-buffered in LDS with a register prefetch of
 //    the next tile; padded LDS pitches keep the 16-byte reads conflict-free;
 //  * workgroups are numbered longest-first (the causal triangle's last query
@@ -39,20 +46,21 @@ template <int D, int HPW>
 struct AttnCfg {
   static constexpr int ROWS = 32 * kAttnWaves / HPW;    // query rows per workgroup
   static constexpr int KP = D + 8;                       // K tile pitch (bf16 elements)
-  static constexpr int VP = kBN + 8;                     // V^T tile pitch
+  static constexpr int VP = kBN;                         // V^T tile pitch (128 B rows, swizzled)
   static constexpr int KPIECES = kBN * D / 8;            // 16-byte pieces of a K tile
   static constexpr int K_PER_T = KPIECES / (kAttnWaves * 64);
   static constexpr int DC = D / 8;                       // 8-wide d chunks
   static constexpr int VGROUPS = kBN / 4;                // 4-key groups per tile
   static_assert(KPIECES % (kAttnWaves * 64) == 0, "K pieces");
-  static_assert(VGROUPS * DC <= kAttnWaves * 64, "V staging");
+  static_assert(VGROUPS * DC <= kAttnWaves * 64 && VGROUPS == 16, "V staging");
 };
 
 template <int D, int HPW>
 __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
     int m, int hq, int hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos, const float* __restrict__ s_kept,
-    const float* __restrict__ gain, float c_scale, uint16_t* __restrict__ out, int n_qtiles) {
+    const float* __restrict__ gain, float c_scale, float bias_scale, float rescale_thr,
+    uint16_t* __restrict__ out, int n_qtiles) {
   using C = AttnCfg<D, HPW>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN][C::KP];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D][C::VP];
@@ -91,7 +99,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
   const bool use_bias = s_kept != nullptr;
   float hgain[HPW];
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) hgain[j] = use_bias ? gain[head0 + j] * kLog2e : 0.f;
+  for (int j = 0; j < HPW; ++j) hgain[j] = use_bias ? gain[head0 + j] * bias_scale : 0.f;
 
   // ---- K/V tile staging (global -> registers -> LDS) ----
   const int rows_end = min(m, (qt + 1) * C::ROWS);
@@ -100,8 +108,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
   u32x4 vreg[4];
   float sreg = 0.f;
   int32_t preg = INT32_MAX;
-  const int vkg = tid / C::DC, vdc = tid % C::DC;       // V staging: 4-key group, d chunk
-  const bool v_stager = vkg < C::VGROUPS;
+  const int vkg = tid % C::VGROUPS, vdc = tid / C::VGROUPS;   // V staging: 4-key group, d chunk
+  const bool v_stager = vdc < C::DC;
 
   auto load_tile = [&](int t) {
     const int kb = t * kBN;
@@ -135,17 +143,20 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
       *reinterpret_cast<u32x4*>(&k_lds[buf][r][8 * c]) = kreg[i];
     }
     if (v_stager) {
-      // 4 keys x 8 d -> 8 rows of V^T, 4 keys (8 bytes) each, key groups of every
-      // 16-key block stored in the order [0, 2, 1, 3]
+      // 4 keys x 8 d -> 8 rows of V^T, 4 keys (8 bytes) each.  Adjacent d-chunks visit
+      // the 8 rows in opposite parity order so one instruction writes both bank halves.
       const int g4 = vkg & 3;
       const int col = (vkg >> 2) * 16 + ((g4 == 1) ? 8 : (g4 == 2) ? 4 : (g4 == 3 ? 12 : 0));
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1, sh = (e & 1) * 16;
-        const uint32_t a0 = (vreg[0][w] >> sh) & 0xffffu, a1 = (vreg[1][w] >> sh) & 0xffffu;
-        const uint32_t a2 = (vreg[2][w] >> sh) & 0xffffu, a3 = (vreg[3][w] >> sh) & 0xffffu;
-        u32x2 pk = {a0 | (a1 << 16), a2 | (a3 << 16)};
-        *reinterpret_cast<u32x2*>(&vt_lds[buf][8 * vdc + e][col]) = pk;
+        const int e2 = e ^ (vdc & 1);
+        const int d = 8 * vdc + e2;
+        const int w = e2 >> 1;
+        const uint32_t sel = (e2 & 1) ? 0x07060302u : 0x05040100u;
+        u32x2 pk = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel),
+                    __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel)};
+        const int pchunk = (col >> 3) ^ ((d >> 1) & 7);
+        *reinterpret_cast<u32x2*>(&vt_lds[buf][d][8 * pchunk + (col & 7)]) = pk;
       }
     }
     if (tid < kBN) {
@@ -160,7 +171,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
   for (int u = 0; u < D / 32; ++u)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[u][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, neg_mc = 0.f;
 
   load_tile(0);
   store_tile(0);
@@ -172,12 +183,24 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
     if (t + 1 < n_tiles) load_tile(t + 1);
 
     if (wave_live && kb <= wave_last) {
-      // S^T tile: keys kb + 32*kt + (8*(i/4) + 4*half + i%4), query = row
+      // S^T tile: keys kb + 32*kt + (8*g + 4*half + r) for register 4g+r, query = row.
+      // The accumulator starts at the key bias (q.k units), so S = q.k + bias.
       f32x16 sacc[2];
+      if (use_bias) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 bb = *reinterpret_cast<const f32x4*>(&bias_lds[buf][hh][32 * kt + 8 * g + 4 * half]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[kt][4 * g + r] = bb[r];
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+      }
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
@@ -186,65 +209,73 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
           sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
         }
       }
-      const bool need_mask = (kb + kBN - 1 > q0) || (kb + kBN > m);
-      float mt = -INFINITY;
+      if ((kb + kBN - 1 > q0) || (kb + kBN > m)) {   // tile straddles the causal edge or the end
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int kk = 32 * kt + 8 * g + 4 * half;
-          const f32x4 bb = *reinterpret_cast<const f32x4*>(&bias_lds[buf][hh][kk]);
+          for (int g = 0; g < 4; ++g) {
+            const int kk = 32 * kt + 8 * g + 4 * half;
+            typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+            const i32x4 kp = *reinterpret_cast<const i32x4*>(&kpos_lds[buf][kk]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float x = fmaf(sacc[kt][4 * g + r], c_scale, bb[r]);
-            if (need_mask && kpos_lds[buf][kk + r] > qpos) x = -INFINITY;
-            sacc[kt][4 * g + r] = x;
-            mt = fmaxf(mt, x);
+            for (int r = 0; r < 4; ++r)
+              if (kp[r] > qpos) sacc[kt][4 * g + r] = -INFINITY;
           }
-        }
-      mt = fmaxf(mt, swap_halves(mt));
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      float lsum = 0.f;
+      }
+      float mt = sacc[0][0];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(sacc[kt][i] - m_new);
-          sacc[kt][i] = p;
-          lsum += p;
-        }
-      l_run = fmaf(l_run, alpha, lsum);
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kt][i]);
+      mt = pair_max(mt);
+      // lazy rescale: move the running max only when this tile exceeds it by > 2^8
+      if (__ballot(mt > m_run + rescale_thr)) {
+        const float m_new = fmaxf(m_run, mt);
+        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_scale);
+        m_run = m_new;
+        neg_mc = -m_new * c_scale;
+        l_run *= alpha;
 #pragma unroll
-      for (int u = 0; u < D / 32; ++u)
+        for (int u = 0; u < D / 32; ++u)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[u][i] *= alpha;
-      // P^T fragments: step s2 covers keys 16*s2 .. +15; element e of lane half h is
-      // key 16*s2 + (e < 4 ? 4h + e : 8 + 4h + e - 4) = registers 8*(s2%2) + e of tile s2/2
+          for (int i = 0; i < 16; ++i) oacc[u][i] *= alpha;
+      }
+      // P = exp2(S c - m c), packed to bf16 as the B operand of the P.V step: step s2
+      // covers keys 16*s2 .. +15; element e of lane half h is key 16*s2 + (e < 4 ? 4h + e :
+      // 8 + 4h + e - 4) = register 8*(s2%2) + e of tile s2/2
       bf16x8 pf[4];
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) {
-        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-        u32x4_t w;
+        u32x4 w;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          w[e2] = pack_bf16x2(sacc[s2 >> 1][8 * (s2 & 1) + 2 * e2], sacc[s2 >> 1][8 * (s2 & 1) + 2 * e2 + 1]);
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s2 >> 1][8 * (s2 & 1) + 2 * e2], c_scale, neg_mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s2 >> 1][8 * (s2 & 1) + 2 * e2 + 1], c_scale, neg_mc));
+          // (bit-cast a scalar, not the vector element: clang folds the latter to element 0)
+          const uint32_t pk = pack_bf16x2(p0, p1);
+          w[e2] = pk;
+          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, l_run, false);
+        }
         pf[s2] = __builtin_bit_cast(bf16x8, w);
       }
 #pragma unroll
-      for (int u = 0; u < D / 32; ++u)
+      for (int u = 0; u < D / 32; ++u) {
+        const int d = 32 * u + l32;
+        const int sw = (d >> 1) & 7;
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt_lds[buf][32 * u + l32][16 * s2 + 8 * half]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt_lds[buf][d][8 * ((2 * s2 + half) ^ sw)]);
           oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s2], oacc[u], 0, 0, 0);
         }
+      }
     }
     if (t + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
   }
 
-  const float l_tot = l_run + swap_halves(l_run);   // wave-uniform exchange
+  const float l_tot = pair_sum(l_run);   // wave-uniform exchange
   if (row < m) {
     const float inv = 1.0f / l_tot;
     uint16_t* orow = out + ((int64_t)row * hq + head) * D;
@@ -332,15 +363,15 @@ __global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(int m, int hq, int h
 template <int D, int HPW>
 static tg_status launch_attn_bf16(int m, int hq, int hkv, const void* q, const void* k, const void* v,
                                   const int32_t* pos, const float* s_kept, const float* gain, float c_scale,
-                                  void* out, hipStream_t st) {
+                                  float bias_scale, void* out, hipStream_t st) {
   using C = AttnCfg<D, HPW>;
   const int n_qtiles = (m + C::ROWS - 1) / C::ROWS;
   const int64_t grid = (int64_t)n_qtiles * (hq / HPW);
   if (grid > INT32_MAX) return TG_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((attn_bf16_kernel<D, HPW>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0, st, m, hq, hkv,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, static_cast<uint16_t*>(out),
-                     n_qtiles);
+                     static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, bias_scale,
+                     8.0f / c_scale, static_cast<uint16_t*>(out), n_qtiles);
   TG_CHECK_LAUNCH();
   return TG_OK;
 }
@@ -348,11 +379,13 @@ static tg_status launch_attn_bf16(int m, int hq, int hkv, const void* q, const v
 template <int D>
 static tg_status dispatch_attn_bf16(int m, int hq, int hkv, const void* q, const void* k, const void* v,
                                     const int32_t* pos, const float* s_kept, const float* gain, float c_scale,
-                                    void* out, hipStream_t st) {
+                                    float bias_scale, void* out, hipStream_t st) {
   const int group = hq / hkv;
-  if (group % 4 == 0) return launch_attn_bf16<D, 4>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, out, st);
-  if (group % 2 == 0) return launch_attn_bf16<D, 2>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, out, st);
-  return launch_attn_bf16<D, 1>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, out, st);
+  if (group % 4 == 0)
+    return launch_attn_bf16<D, 4>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, st);
+  if (group % 2 == 0)
+    return launch_attn_bf16<D, 2>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, st);
+  return launch_attn_bf16<D, 1>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, st);
 }
 
 }  // namespace tg
@@ -375,11 +408,14 @@ extern "C" tg_status tg_gated_attention(int32_t dtype, int64_t m, int32_t n_q_he
   if (align & 15u) return TG_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float c_scale = static_cast<float>(1.4426950408889634 / (std::sqrt((double)head_dim) * (double)tau));
+  const float bias_scale = static_cast<float>(std::sqrt((double)head_dim) * (double)tau);   // bias in q.k units
   const int mm = static_cast<int>(m);
   if (dtype == TG_BF16) {
     return head_dim == 128
-               ? dispatch_attn_bf16<128>(mm, n_q_heads, n_kv_heads, q, k, v, pos, s_kept, gain, c_scale, out, st)
-               : dispatch_attn_bf16<64>(mm, n_q_heads, n_kv_heads, q, k, v, pos, s_kept, gain, c_scale, out, st);
+               ? dispatch_attn_bf16<128>(mm, n_q_heads, n_kv_heads, q, k, v, pos, s_kept, gain, c_scale,
+                                         bias_scale, out, st)
+               : dispatch_attn_bf16<64>(mm, n_q_heads, n_kv_heads, q, k, v, pos, s_kept, gain, c_scale,
+                                        bias_scale, out, st);
   }
   const dim3 grid((mm + kF32Rows - 1) / kF32Rows, n_q_heads);
   if (head_dim == 128)

@@ -56,6 +56,18 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max / sum of the values held by lanes l and l^32, in every lane.  v_permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its second, so
+// with both operands = x each lane ends up holding {x[l], x[l^32]} (in some order).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
 }  // namespace tg
