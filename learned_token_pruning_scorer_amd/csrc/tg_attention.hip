@@ -111,28 +111,30 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
   const int vkg = tid % C::VGROUPS, vdc = tid / C::VGROUPS;   // V staging: 4-key group, d chunk
   const bool v_stager = vdc < C::DC;
 
+  // Keys past the end are clamped to the last row: their loads stay in bounds and
+  // unconditional, and their position INT32_MAX masks them out (P = 0 exactly).
   auto load_tile = [&](int t) {
     const int kb = t * kBN;
 #pragma unroll
     for (int i = 0; i < C::K_PER_T; ++i) {
       const int p = tid + i * kAttnWaves * 64;
       const int r = p / C::DC, c = p % C::DC;
-      const int key = kb + r;
-      kreg[i] = key < m ? *reinterpret_cast<const u32x4*>(k + ((int64_t)key * hkv + kvh) * D + 8 * c)
-                        : u32x4{0u, 0u, 0u, 0u};
+      const int key = min(kb + r, m - 1);
+      kreg[i] = *reinterpret_cast<const u32x4*>(k + ((int64_t)key * hkv + kvh) * D + 8 * c);
     }
     if (v_stager) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int key = kb + 4 * vkg + r;
-        vreg[r] = key < m ? *reinterpret_cast<const u32x4*>(v + ((int64_t)key * hkv + kvh) * D + 8 * vdc)
-                          : u32x4{0u, 0u, 0u, 0u};
+        const int key = min(kb + 4 * vkg + r, m - 1);
+        vreg[r] = *reinterpret_cast<const u32x4*>(v + ((int64_t)key * hkv + kvh) * D + 8 * vdc);
       }
     }
     if (tid < kBN) {
       const int key = kb + tid;
-      sreg = (use_bias && key < m) ? s_kept[key] : 0.f;
-      preg = key < m ? (pos ? pos[key] : key) : INT32_MAX;
+      const int kc = min(key, m - 1);
+      sreg = use_bias ? s_kept[kc] : 0.f;
+      const int32_t pk = pos ? pos[kc] : kc;
+      preg = key < m ? pk : INT32_MAX;
     }
   };
   auto store_tile = [&](int buf) {

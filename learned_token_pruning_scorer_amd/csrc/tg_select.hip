@@ -5,55 +5,90 @@
 // section 事件详情; aisight.pl "TokenGate: Stanford i Berkeley ...", section
 // "Jak to dziala").
 //
-// Scores are mapped to order-preserving uint32 keys.  A radix select over three
-// digits (bits 31..20, 19..8, 7..0) finds the threshold key T, the K-th largest
-// document key, and `need_eq`, how many keys equal to T are kept.  Each digit pass
-// builds a workgroup-local LDS histogram, adds it to a global histogram with
-// atomics, and the last workgroup to finish (a done-counter) scans the global
-// histogram to pick the digit and clears it again.  Compaction then needs, for
-// every position i, two prefix counts: `base` (positions kept outright: outside
-// the document, or key > T) and `eq` (document keys equal to T).  Position i is
-// kept iff base(i) or (eq(i) and eq_before(i) < need_eq), and its output slot is
-// base_before(i) + min(eq_before(i), need_eq).  Ties thus go to the lowest
-// positions, and the output is ascending by construction.
+// One launch does the whole selection.  At most 64 workgroups each own a
+// contiguous chunk of positions (held in registers as keys); they are all
+// resident at once and meet at counted grid barriers between phases.  A barrier
+// is one device-scope atomic per workgroup plus polling -- no cache write-back
+// fence: every value that crosses workgroups (histogram bins, chunk counts) is
+// itself a device-scope atomic, and each thread drains its own atomics before
+// its workgroup arrives.  The wait is bounded, so a grid that is not fully
+// resident (the device shared with other work) cannot hang; a timeout is flagged
+// in the workspace.  Phases:
+//   1-3. radix select over the order-preserving uint32 score keys, three digits
+//        (bits 31..21, 20..10, 9..0): each workgroup histograms its chunk's
+//        document keys that carry the prefix fixed so far into LDS, merges the
+//        non-zero bins into a global histogram with atomics, and after the barrier
+//        every workgroup scans that histogram from the top to fix the next digit.
+//        The result is the threshold key T (the K-th largest document key) and
+//        need_eq, how many keys equal to T are kept;
+//   4.   compaction: position i is kept iff it lies outside the document, or its
+//        key > T, or key == T and fewer than need_eq equal keys precede it.  Its
+//        output slot is base_before(i) + min(eq_before(i), need_eq), from two
+//        prefix counts (positions kept outright, document keys equal to T); the
+//        per-workgroup totals are exchanged at one more barrier.
+// Ties therefore go to the lowest positions and the output is ascending.
+#include <atomic>
+
 #include "tg_common.h"
 
 namespace tg {
 
-constexpr int kSelThreads = 256;
-constexpr int kHistBins01 = 4096;   // digits of passes 0 and 1 (12 bits)
-constexpr int kHistBins2 = 256;     // digit of pass 2 (8 bits)
-constexpr int kCmpPerThread = 4;
-constexpr int kCmpChunk = kSelThreads * kCmpPerThread;   // positions per compaction block
-constexpr int kHistMaxBlocks = 256;
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelMaxBlocks = 64;             // barrier cost grows with the number of workgroups
+constexpr int kSelPosPerBlock = 2048;         // target chunk per workgroup
+constexpr int kSelRegKeys = 8;                // keys per thread kept in registers across phases
+constexpr int kSelMaxBins = 2048;
+constexpr uint32_t kSpinLimit = 1u << 22;     // bounded barrier wait (never reached when co-resident)
 
-struct SelState {         // head of the workspace (64 bytes)
-  uint32_t done[4];       // per-pass done counters (always 0 between calls)
-  uint32_t prefix;        // key bits fixed so far
-  uint32_t rank;          // 1-based rank still wanted among keys with that prefix
-  uint32_t pad[10];
+struct SelState {       // head of the workspace (64 bytes)
+  uint32_t barrier;     // barrier arrivals of the current call (reset by the last workgroup out)
+  uint32_t exit;        // workgroups finished
+  uint32_t timeout;     // set if a barrier wait ever gave up
+  uint32_t pad[13];
 };
 
 struct SelLayout {
-  size_t state = 0;
-  size_t hist0 = 64;
-  size_t hist1 = hist0 + kHistBins01 * 4;
-  size_t hist2 = hist1 + kHistBins01 * 4;
-  size_t counts = hist2 + kHistBins2 * 4;
-  size_t bytes(int64_t n) const {
-    const int64_t blocks = (n + kCmpChunk - 1) / kCmpChunk;
-    const size_t end = counts + (size_t)blocks * 2 * sizeof(uint32_t);
-    return (end + 255) & ~size_t(255);
-  }
+  static constexpr size_t state = 0;
+  static constexpr size_t hist0 = 64;
+  static constexpr size_t hist1 = hist0 + 2048 * 4;
+  static constexpr size_t hist2 = hist1 + 2048 * 4;
+  static constexpr size_t counts = hist2 + 1024 * 4;
+  static constexpr size_t bytes = (counts + 2 * kSelMaxBlocks * 4 + 255) & ~size_t(255);
 };
 
 __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Block-wide exclusive scan of one uint32 per thread (kSelThreads threads); returns
-// the exclusive prefix and writes the block total to *total.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* sh /*[4]*/) {
+__device__ __forceinline__ void st_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until this thread's own outstanding memory operations (the device-scope
+// atomics it issued) have completed.
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// All workgroups of the grid wait here until `target` arrivals have been counted.
+__device__ __forceinline__ void grid_barrier(SelState* st, uint32_t target) {
+  drain_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicAdd(&st->barrier, 1u);
+    uint32_t spins = 0;
+    while (ld_agent(&st->barrier) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {             // only if the grid is not fully resident; never hang
+        atomicOr(&st->timeout, 1u);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Exclusive scan of one value per thread over the workgroup; *total gets the sum.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total, uint32_t* sh /*[kSelWaves]*/) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t incl = v;
 #pragma unroll
@@ -65,7 +100,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total,
   __syncthreads();
   uint32_t wbase = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kSelThreads / 64; ++w) {
+  for (int w = 0; w < kSelWaves; ++w) {
     const uint32_t s = sh[w];
     wbase += (w < wave) ? s : 0u;
     tot += s;
@@ -75,161 +110,191 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* total,
   return wbase + incl - v;
 }
 
-// One radix digit pass over the document keys.
-template <int PASS>
-__global__ __launch_bounds__(kSelThreads) void sel_hist_kernel(const float* __restrict__ scores,
-                                                               int doc_begin, int doc_len,
-                                                               uint32_t k_eff, SelState* st,
-                                                               uint32_t* hist) {
-  constexpr int BINS = PASS == 2 ? kHistBins2 : kHistBins01;
-  __shared__ uint32_t lh[BINS];
-  __shared__ uint32_t sh_scan[4];
-  __shared__ int sh_last;
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* sh /*[kSelWaves]*/) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t tot = 0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) tot += sh[w];
+  __syncthreads();
+  return tot;
+}
+
+// mode 0: keep no document token; 1: keep the whole document; 2: select min(k, D) of it.
+__global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(const float* __restrict__ scores, int n,
+                                                                int doc_begin, int doc_end, uint32_t k_eff,
+                                                                int mode, int chunk, uint32_t m, char* ws,
+                                                                int32_t* __restrict__ kept) {
+  __shared__ uint32_t lh[kSelMaxBins];
+  __shared__ uint32_t sh[kSelWaves];
+  __shared__ uint32_t sh_prefix, sh_rank;
+  SelState* st = reinterpret_cast<SelState*>(ws + SelLayout::state);
+  uint32_t* hist0 = reinterpret_cast<uint32_t*>(ws + SelLayout::hist0);
+  uint32_t* hist1 = reinterpret_cast<uint32_t*>(ws + SelLayout::hist1);
+  uint32_t* hist2 = reinterpret_cast<uint32_t*>(ws + SelLayout::hist2);
+  uint32_t* counts = reinterpret_cast<uint32_t*>(ws + SelLayout::counts);
   const int tid = threadIdx.x;
-  for (int i = tid; i < BINS; i += kSelThreads) lh[i] = 0;
-  __syncthreads();
-  const uint32_t prefix = PASS == 0 ? 0u : st->prefix;
-  for (int i = blockIdx.x * kSelThreads + tid; i < doc_len; i += gridDim.x * kSelThreads) {
-    const uint32_t key = score_key(scores[doc_begin + i]);
-    if (PASS == 0) {
-      atomicAdd(&lh[key >> 20], 1u);
-    } else if (PASS == 1) {
-      if ((key >> 20) == prefix) atomicAdd(&lh[(key >> 8) & 0xfffu], 1u);
-    } else {
-      if ((key >> 8) == prefix) atomicAdd(&lh[key & 0xffu], 1u);
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < BINS; i += kSelThreads)
-    if (lh[i]) atomicAdd(&hist[i], lh[i]);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sh_last = (atomicAdd(&st->done[PASS], 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!sh_last) return;
-  __threadfence();
+  const uint32_t G = gridDim.x;
+  const int c0 = blockIdx.x * chunk;
+  const int c1 = min(n, c0 + chunk);
 
-  // Last block: walk the bins from the top (largest keys) down to the one that
-  // holds the rank-th largest key among those with the current prefix.
-  const uint32_t rank = PASS == 0 ? k_eff : st->rank;
-  constexpr int PER = BINS / kSelThreads;
-  uint32_t c[PER];
-  uint32_t local = 0;
+  // The chunk's keys: position c0 + tid + 512*r is keys[r], kept in registers when the
+  // chunk fits (up to 64 x 512 x 8 = 262144 positions); larger chunks re-read scores.
+  const bool in_regs = c1 - c0 <= kSelThreads * kSelRegKeys;
+  uint32_t keys[kSelRegKeys];
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
-    c[p] = ld_agent(&hist[BINS - 1 - (tid * PER + p)]);
-    local += c[p];
+  for (int r = 0; r < kSelRegKeys; ++r) {
+    const int i = c0 + tid + r * kSelThreads;
+    keys[r] = (in_regs && i < c1) ? score_key(scores[i]) : 0u;
   }
-  uint32_t total;
-  uint32_t above = block_excl_scan(local, &total, sh_scan);
-  if (above < rank && rank <= above + local) {
+  // f(i, key) for every position of the chunk held by this thread
+  auto for_chunk = [&](auto&& f) {
+    if (in_regs) {
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      if (rank <= above + c[p]) {
-        const uint32_t bin = BINS - 1 - (tid * PER + p);
-        st->prefix = PASS == 0 ? bin : (PASS == 1 ? (prefix << 12) | bin : (prefix << 8) | bin);
-        st->rank = rank - above;
-        break;
+      for (int r = 0; r < kSelRegKeys; ++r) {
+        const int i = c0 + tid + r * kSelThreads;
+        if (i < c1) f(i, keys[r]);
       }
-      above += c[p];
+    } else {
+      for (int i = c0 + tid; i < c1; i += kSelThreads) f(i, score_key(scores[i]));
+    }
+  };
+
+  uint32_t T = 0xffffffffu, need = 0u;   // mode 0: no key reaches 0xffffffff
+  if (mode == 1) { T = 0u; need = 0xffffffffu; }
+  uint32_t barriers = 0;
+  if (mode == 2) {
+    uint32_t prefix = 0u, rank = k_eff;
+#pragma unroll 1
+    for (int p = 0; p < 3; ++p) {
+      const int shift = p == 0 ? 21 : (p == 1 ? 10 : 0);
+      const int bits = p == 2 ? 10 : 11;
+      const uint32_t bins = 1u << bits;
+      uint32_t* hist = p == 0 ? hist0 : (p == 1 ? hist1 : hist2);
+      for (uint32_t i = tid; i < bins; i += kSelThreads) lh[i] = 0u;
+      __syncthreads();
+      for_chunk([&](int i, uint32_t key) {
+        if (i >= doc_begin && i < doc_end && (p == 0 || (key >> (shift + bits)) == prefix))
+          atomicAdd(&lh[(key >> shift) & (bins - 1)], 1u);
+      });
+      __syncthreads();
+      for (uint32_t i = tid; i < bins; i += kSelThreads)
+        if (lh[i]) atomicAdd(&hist[i], lh[i]);
+      grid_barrier(st, ++barriers * G);
+      // every workgroup finished reading the previous digit's histogram before this barrier
+      if (p == 1 && blockIdx.x == 0)
+        for (uint32_t i = tid; i < 2048u; i += kSelThreads) hist0[i] = 0u;
+      if (p == 2 && blockIdx.x == 0)
+        for (uint32_t i = tid; i < 2048u; i += kSelThreads) hist1[i] = 0u;
+      // walk the bins from the top (largest keys) to the one holding the rank-th key
+      const uint32_t per = bins / kSelThreads;   // 4 or 2
+      uint32_t c[4] = {0u, 0u, 0u, 0u};
+      uint32_t local = 0u;
+#pragma unroll
+      for (uint32_t q = 0; q < 4; ++q) {
+        if (q < per) {
+          c[q] = ld_agent(&hist[bins - 1 - (tid * per + q)]);
+          local += c[q];
+        }
+      }
+      uint32_t total;
+      uint32_t above = block_excl_scan(local, &total, sh);
+      if (above < rank && rank <= above + local) {
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q) {
+          if (q < per) {
+            if (rank <= above + c[q]) {
+              sh_prefix = (prefix << bits) | (bins - 1 - (tid * per + q));
+              sh_rank = rank - above;
+              break;
+            }
+            above += c[q];
+          }
+        }
+      }
+      __syncthreads();
+      prefix = sh_prefix;
+      rank = sh_rank;
+    }
+    T = prefix;
+    need = rank;
+  }
+
+  // ---- compaction ----
+  // flags of a position: fb = kept outright (outside the document, or key > T); fe = key == T
+  auto flags = [&](int i, uint32_t key, uint32_t* fb, uint32_t* fe) {
+    const bool doc = i >= doc_begin && i < doc_end;
+    *fb = (!doc || key > T) ? 1u : 0u;
+    *fe = (doc && key == T) ? 1u : 0u;
+  };
+  uint32_t nb = 0u, ne = 0u;
+  for_chunk([&](int i, uint32_t key) {
+    uint32_t fb, fe;
+    flags(i, key, &fb, &fe);
+    nb += fb;
+    ne += fe;
+  });
+  nb = block_sum(nb, sh);
+  ne = block_sum(ne, sh);
+  if (tid == 0) {
+    st_agent(&counts[2 * blockIdx.x], nb);
+    st_agent(&counts[2 * blockIdx.x + 1], ne);
+  }
+  grid_barrier(st, ++barriers * G);
+  if (mode == 2 && blockIdx.x == 0)
+    for (int i = tid; i < 1024; i += kSelThreads) hist2[i] = 0u;
+  uint32_t pb = 0u, pe = 0u;
+  for (uint32_t b = tid; b < blockIdx.x; b += kSelThreads) {
+    pb += ld_agent(&counts[2 * b]);
+    pe += ld_agent(&counts[2 * b + 1]);
+  }
+  uint32_t base_before = block_sum(pb, sh);
+  uint32_t eq_before = block_sum(pe, sh);
+  // one round of 512 positions: scan the flags and write the kept positions
+  auto round = [&](int i, uint32_t key) {
+    uint32_t fb = 0u, fe = 0u;
+    if (i < c1) flags(i, key, &fb, &fe);
+    uint32_t tot;   // both counts in one scan: each is <= kSelThreads
+    const uint32_t ex = block_excl_scan(fb | (fe << 16), &tot, sh);
+    const uint32_t bb = base_before + (ex & 0xffffu), eb = eq_before + (ex >> 16);
+    const uint32_t slot = bb + min(eb, need);
+    if ((fb || (fe && eb < need)) && slot < m) kept[slot] = i;   // slot < m always holds
+    base_before += tot & 0xffffu;
+    eq_before += tot >> 16;
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int r = 0; r < kSelRegKeys; ++r)
+      if (c0 + r * kSelThreads < c1) round(c0 + tid + r * kSelThreads, keys[r]);   // uniform condition
+  } else {
+    for (int r0 = c0; r0 < c1; r0 += kSelThreads) {
+      const int i = r0 + tid;
+      round(i, i < c1 ? score_key(scores[i]) : 0u);
     }
   }
-  for (int i = tid; i < BINS; i += kSelThreads) hist[i] = 0u;
-  if (tid == 0) st->done[PASS] = 0u;
-}
-
-// Selection outcome as (threshold key, quota of keys equal to it).
-//   mode 0: keep no document token; mode 1: keep the whole document; mode 2: from the passes.
-__device__ __forceinline__ void sel_threshold(int mode, const SelState* st, uint32_t* T, uint32_t* need) {
-  if (mode == 0) { *T = 0xffffffffu; *need = 0u; }          // no key reaches 0xffffffff
-  else if (mode == 1) { *T = 0u; *need = 0xffffffffu; }     // every key >= 0 = T, no quota
-  else { *T = st->prefix; *need = st->rank; }
-}
-
-__device__ __forceinline__ void cmp_flags(const float* scores, int i, int n, int doc_begin, int doc_end,
-                                          uint32_t T, uint32_t* base, uint32_t* eq) {
-  *base = 0u; *eq = 0u;
-  if (i >= n) return;
-  if (i < doc_begin || i >= doc_end) { *base = 1u; return; }
-  const uint32_t key = score_key(scores[i]);
-  *base = key > T;
-  *eq = key == T;
-}
-
-__global__ __launch_bounds__(kSelThreads) void sel_count_kernel(const float* __restrict__ scores, int n,
-                                                                int doc_begin, int doc_end, int mode,
-                                                                const SelState* st, uint32_t* counts) {
-  __shared__ uint32_t sh[2][4];
-  uint32_t T, need;
-  sel_threshold(mode, st, &T, &need);
-  const int i0 = blockIdx.x * kCmpChunk + threadIdx.x * kCmpPerThread;
-  uint32_t nb = 0, ne = 0;
-#pragma unroll
-  for (int r = 0; r < kCmpPerThread; ++r) {
-    uint32_t b, e;
-    cmp_flags(scores, i0 + r, n, doc_begin, doc_end, T, &b, &e);
-    nb += b; ne += e;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    nb += __shfl_xor(nb, o, 64);
-    ne += __shfl_xor(ne, o, 64);
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) { sh[0][wave] = nb; sh[1][wave] = ne; }
+  // the last workgroup out resets the barrier counters for the next call
   __syncthreads();
-  if (threadIdx.x == 0) {
-    counts[2 * blockIdx.x] = sh[0][0] + sh[0][1] + sh[0][2] + sh[0][3];
-    counts[2 * blockIdx.x + 1] = sh[1][0] + sh[1][1] + sh[1][2] + sh[1][3];
+  if (tid == 0 && atomicAdd(&st->exit, 1u) == G - 1) {
+    st->barrier = 0u;
+    st->exit = 0u;
   }
 }
 
-__global__ __launch_bounds__(kSelThreads) void sel_write_kernel(const float* __restrict__ scores, int n,
-                                                                int doc_begin, int doc_end, int mode,
-                                                                const SelState* st,
-                                                                const uint32_t* __restrict__ counts,
-                                                                int32_t* __restrict__ kept, uint32_t m) {
-  __shared__ uint32_t sh_scan[4];
-  __shared__ uint32_t sh_red[2][4];
-  uint32_t T, need;
-  sel_threshold(mode, st, &T, &need);
-  // offsets of this block: sums of the counts of all earlier blocks
-  uint32_t pb = 0, pe = 0;
-  for (int b = threadIdx.x; b < (int)blockIdx.x; b += kSelThreads) {
-    pb += counts[2 * b];
-    pe += counts[2 * b + 1];
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    pb += __shfl_xor(pb, o, 64);
-    pe += __shfl_xor(pe, o, 64);
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) { sh_red[0][wave] = pb; sh_red[1][wave] = pe; }
-  __syncthreads();
-  const uint32_t block_base = sh_red[0][0] + sh_red[0][1] + sh_red[0][2] + sh_red[0][3];
-  const uint32_t block_eq = sh_red[1][0] + sh_red[1][1] + sh_red[1][2] + sh_red[1][3];
-
-  const int i0 = blockIdx.x * kCmpChunk + threadIdx.x * kCmpPerThread;
-  uint32_t fb[kCmpPerThread], fe[kCmpPerThread], nb = 0, ne = 0;
-#pragma unroll
-  for (int r = 0; r < kCmpPerThread; ++r) {
-    cmp_flags(scores, i0 + r, n, doc_begin, doc_end, T, &fb[r], &fe[r]);
-    nb += fb[r]; ne += fe[r];
-  }
-  // pack both counts in one 32-bit scan: each is <= kCmpChunk (< 2^16)
-  uint32_t tot;
-  const uint32_t ex = block_excl_scan(nb | (ne << 16), &tot, sh_scan);
-  uint32_t base_before = block_base + (ex & 0xffffu);
-  uint32_t eq_before = block_eq + (ex >> 16);
-#pragma unroll
-  for (int r = 0; r < kCmpPerThread; ++r) {
-    const bool keep = fb[r] || (fe[r] && eq_before < need);
-    const uint32_t slot = base_before + min(eq_before, need);
-    if (keep && slot < m) kept[slot] = i0 + r;   // slot < m always holds; the guard is defensive
-    base_before += fb[r];
-    eq_before += fe[r];
-  }
+// Workgroups of sel_fused_kernel that fit on `device` at once (cached).
+static int coresident_blocks(int device) {
+  static std::atomic<int> cache[64];
+  if (device < 0 || device >= 64) return 0;
+  int v = cache[device].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sel_fused_kernel, kSelThreads, 0) != hipSuccess)
+    return 0;
+  v = cus * per_cu;
+  cache[device].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 }  // namespace tg
@@ -242,7 +307,7 @@ extern "C" int64_t tg_num_kept(int64_t n, int64_t doc_begin, int64_t doc_end, in
 
 extern "C" size_t tg_select_workspace_bytes(int64_t n) {
   if (n < 0) return 0;
-  return tg::SelLayout().bytes(n);
+  return tg::SelLayout::bytes;
 }
 
 extern "C" tg_status tg_select_topk(int64_t n, const float* scores, int64_t doc_begin, int64_t doc_end,
@@ -250,46 +315,32 @@ extern "C" tg_status tg_select_topk(int64_t n, const float* scores, int64_t doc_
                                     void* stream) {
   using namespace tg;
   if (n <= 0 || n > INT32_MAX || tg_num_kept(n, doc_begin, doc_end, k) < 0) return TG_ERR_INVALID_ARG;
-  if (tg_num_kept(n, doc_begin, doc_end, k) == 0) return TG_OK;   // nothing kept, nothing to write
+  const int64_t m64 = tg_num_kept(n, doc_begin, doc_end, k);
+  if (m64 == 0) return TG_OK;   // nothing kept, nothing to write
   if (!scores || !kept_idx || !workspace) return TG_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return TG_ERR_INVALID_ARG;
-  const SelLayout L;
-  if (workspace_bytes < L.bytes(n)) return TG_ERR_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  SelState* state = reinterpret_cast<SelState*>(ws + L.state);
-  uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);
-  const int nn = static_cast<int>(n), db = static_cast<int>(doc_begin), de = static_cast<int>(doc_end);
+  if (workspace_bytes < SelLayout::bytes) return TG_ERR_WORKSPACE;
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess) return TG_ERR_HIP;
+  const int cap = coresident_blocks(device);
+  if (cap <= 0) return TG_ERR_HIP;
+  int64_t grid = (n + kSelPosPerBlock - 1) / kSelPosPerBlock;
+  grid = grid < 1 ? 1 : grid;
+  grid = grid > kSelMaxBlocks ? kSelMaxBlocks : grid;
+  grid = grid > cap ? cap : grid;
+  int64_t chunk = (n + grid - 1) / grid;
+  chunk = (chunk + kSelThreads - 1) / kSelThreads * kSelThreads;
+  grid = (n + chunk - 1) / chunk;
+
   const int64_t d = doc_end - doc_begin;
   const int64_t k_eff = k < d ? k : d;
-  int mode;
-  if (k_eff == 0) {
-    mode = 0;
-  } else if (k_eff == d) {
-    mode = 1;
-  } else {
-    mode = 2;
-    const int want = static_cast<int>((d + kSelThreads * 8 - 1) / (kSelThreads * 8));
-    const int grid = want < 1 ? 1 : (want > kHistMaxBlocks ? kHistMaxBlocks : want);
-    const int dl = static_cast<int>(d);
-    const uint32_t ke = static_cast<uint32_t>(k_eff);
-    hipLaunchKernelGGL(sel_hist_kernel<0>, dim3(grid), dim3(kSelThreads), 0, st, scores, db, dl, ke, state,
-                       reinterpret_cast<uint32_t*>(ws + L.hist0));
-    TG_CHECK_LAUNCH();
-    hipLaunchKernelGGL(sel_hist_kernel<1>, dim3(grid), dim3(kSelThreads), 0, st, scores, db, dl, ke, state,
-                       reinterpret_cast<uint32_t*>(ws + L.hist1));
-    TG_CHECK_LAUNCH();
-    hipLaunchKernelGGL(sel_hist_kernel<2>, dim3(grid), dim3(kSelThreads), 0, st, scores, db, dl, ke, state,
-                       reinterpret_cast<uint32_t*>(ws + L.hist2));
-    TG_CHECK_LAUNCH();
-  }
-  const int cblocks = static_cast<int>((n + kCmpChunk - 1) / kCmpChunk);
-  hipLaunchKernelGGL(sel_count_kernel, dim3(cblocks), dim3(kSelThreads), 0, st, scores, nn, db, de, mode,
-                     state, counts);
-  TG_CHECK_LAUNCH();
-  const uint32_t m = static_cast<uint32_t>(tg_num_kept(n, doc_begin, doc_end, k));
-  hipLaunchKernelGGL(sel_write_kernel, dim3(cblocks), dim3(kSelThreads), 0, st, scores, nn, db, de, mode,
-                     state, counts, kept_idx, m);
+  int mode = k_eff == 0 ? 0 : (k_eff == d ? 1 : 2);
+  const int nn = static_cast<int>(n), db = static_cast<int>(doc_begin), de = static_cast<int>(doc_end);
+  const uint32_t ke = static_cast<uint32_t>(k_eff), m = static_cast<uint32_t>(m64);
+  const int ch = static_cast<int>(chunk);
+  char* ws = static_cast<char*>(workspace);
+  hipLaunchKernelGGL(sel_fused_kernel, dim3(static_cast<unsigned>(grid)), dim3(kSelThreads), 0,
+                     static_cast<hipStream_t>(stream), scores, nn, db, de, ke, mode, ch, m, ws, kept_idx);
   TG_CHECK_LAUNCH();
   return TG_OK;
 }

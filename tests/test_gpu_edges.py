@@ -58,9 +58,10 @@ def test_select_workspace_reuse_across_sizes():
         kept = binding.tg_select_topk(torch.from_numpy(s.astype(np.float32)).cuda(), 5, n - 5, k, workspace=ws)
         assert np.array_equal(kept.cpu().numpy().astype(np.int64), oracle.select_topk(s, 5, n - 5, k))
     torch.cuda.synchronize()
-    # done-counters (bytes 0..15) and the three digit histograms are back at zero
-    assert int(ws[:16].count_nonzero()) == 0
-    assert int(ws[64:64 + 4 * (4096 + 4096 + 256)].count_nonzero()) == 0
+    # barrier counters (bytes 0..7) and the three digit histograms (2048 + 2048 + 1024 bins)
+    # are back at zero; the barrier-timeout flag (bytes 8..11) was never raised
+    assert int(ws[:12].count_nonzero()) == 0
+    assert int(ws[64:64 + 4 * (2048 + 2048 + 1024)].count_nonzero()) == 0
 
 
 # --------------------------------------------------------------------------- scorer
