@@ -12,6 +12,11 @@
 //  * a workgroup = 4 waves = 32 query rows x 4 (row-block, head) slots; the heads of
 //    one workgroup share a key/value head (grouped-query attention), so each K/V
 //    tile staged in LDS serves every wave;
+//  * K and V tiles of 64 keys go from HBM straight into LDS (global_load_lds, 16
+//    bytes per lane: no staging registers, no VALU), double-buffered, with the next
+//    tile in flight while the current one is consumed.  Both keep the natural
+//    [key][d] layout with the 16-byte chunks of each row XOR-swizzled by the row,
+//    chosen so that the operand reads below are bank-conflict free;
 //  * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16: a
 //    lane then owns ONE query and 16 keys per 32x32 tile, so the row max / row sum
 //    are in-register plus one exchange between the two lane halves;
@@ -23,14 +28,11 @@
 //    when a tile's max exceeds it by more than 8 in the base-2 exponent, so P stays
 //    below 2^8 and most tiles skip the O rescale;
 //  * P^T stays in registers as the B operand of O^T = V^T . P^T; its row sums come
-//    from v_dot2_f32_bf16 on the packed bf16 P that the MFMA consumes.  The 32x32
-//    accumulator layout leaves each lane half with keys {4h..4h+3, 8+4h..8+4h+3}
-//    of every 16-key step, so V is written to LDS transposed (v_perm_b32 packs)
-//    with the key groups of each 16-key block in the order [0, 2, 1, 3] and the
-//    16-byte chunks of each 128-byte V^T row XOR-swizzled by (row/2) mod 8, which
-//    makes both the transposed writes and the operand reads bank-conflict free;
-//  * K/V tiles of 64 keys are double-buffered in LDS with a register prefetch of
-//    the next tile; padded LDS pitches keep the 16-byte reads conflict-free;
+//    from v_dot2_f32_bf16 on the packed bf16 P that the MFMA consumes.  The V^T
+//    operand is read from the [key][d] tile with ds_read_b64_tr_b16: each 16-lane
+//    group addresses 4 keys x 16 d and lane L receives the 4 keys at d0 + L.  The
+//    32x32 accumulator layout leaves each lane half with keys {4h..4h+3,
+//    8+4h..8+4h+3} of every 16-key step, which is what two such reads deliver;
 //  * workgroups are numbered longest-first (the causal triangle's last query
 //    tiles first), and consecutive workgroup ids map to different key/value heads,
 //    which the dispatcher spreads round-robin over the 8 XCDs, so each XCD's L2
@@ -42,17 +44,36 @@ namespace tg {
 constexpr int kAttnWaves = 4;
 constexpr int kBN = 64;   // keys per tile
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// 16 bytes per lane from global memory straight into LDS (lane l -> lds + 16 l; the
+// LDS address must be wave-uniform).  The explicit global address-space cast is needed
+// for the host compilation pass to accept the call.
+__device__ __forceinline__ void lds_load16(const void* gptr, void* lds) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)const_cast<void*>(gptr), (lds_void_t*)lds, 16, 0, 0);
+}
+
+
+// XOR swizzles of the 16-byte chunks of a tile row (row = key within the tile).
+template <int D> struct TileSwz;
+template <> struct TileSwz<128> {   // 256-byte rows: every row starts at bank 0
+  static __device__ __forceinline__ int k(int r) { return r & 15; }
+  static __device__ __forceinline__ int v(int r) { return (r & 3) << 2; }
+};
+template <> struct TileSwz<64> {    // 128-byte rows: consecutive rows alternate bank halves
+  static __device__ __forceinline__ int k(int r) { return (r >> 1) & 7; }
+  static __device__ __forceinline__ int v(int r) { return ((r >> 1) & 1) << 2; }
+};
+
 template <int D, int HPW>
 struct AttnCfg {
   static constexpr int ROWS = 32 * kAttnWaves / HPW;    // query rows per workgroup
-  static constexpr int KP = D + 8;                       // K tile pitch (bf16 elements)
-  static constexpr int VP = kBN;                         // V^T tile pitch (128 B rows, swizzled)
-  static constexpr int KPIECES = kBN * D / 8;            // 16-byte pieces of a K tile
-  static constexpr int K_PER_T = KPIECES / (kAttnWaves * 64);
-  static constexpr int DC = D / 8;                       // 8-wide d chunks
-  static constexpr int VGROUPS = kBN / 4;                // 4-key groups per tile
-  static_assert(KPIECES % (kAttnWaves * 64) == 0, "K pieces");
-  static_assert(VGROUPS * DC <= kAttnWaves * 64 && VGROUPS == 16, "V staging");
+  static constexpr int CPR = D / 8;                      // 16-byte chunks per K/V row
+  static constexpr int ROWS_PER_LOAD = 64 / CPR;         // rows one wave-wide 1 KiB load covers
+  static constexpr int LOADS_PER_WAVE = kBN * CPR / 64 / kAttnWaves;
+  static_assert(LOADS_PER_WAVE >= 1, "tile loads");
 };
 
 template <int D, int HPW>
@@ -62,8 +83,9 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
     const float* __restrict__ gain, float c_scale, float bias_scale, float rescale_thr,
     uint16_t* __restrict__ out, int n_qtiles) {
   using C = AttnCfg<D, HPW>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN][C::KP];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D][C::VP];
+  using Swz = TileSwz<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kBN * D];
   __shared__ __attribute__((aligned(16))) float bias_lds[2][HPW][kBN];
   __shared__ __attribute__((aligned(16))) int32_t kpos_lds[2][kBN];
 
@@ -101,33 +123,30 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
 #pragma unroll
   for (int j = 0; j < HPW; ++j) hgain[j] = use_bias ? gain[head0 + j] * bias_scale : 0.f;
 
-  // ---- K/V tile staging (global -> registers -> LDS) ----
-  const int rows_end = min(m, (qt + 1) * C::ROWS);
-  const int n_tiles = (rows_end + kBN - 1) / kBN;
-  u32x4 kreg[C::K_PER_T];
-  u32x4 vreg[4];
+  // ---- tile loads: K and V global -> LDS directly; bias and positions via registers ----
+  // Wave w's load i covers tile rows ROWS_PER_LOAD*(w*LOADS_PER_WAVE + i) + lane/CPR; lane
+  // writes physical chunk lane%CPR of its row, i.e. logical chunk (lane%CPR) ^ swizzle(row).
+  // Keys past the end are clamped to the last row: the loads stay in bounds, and their
+  // position INT32_MAX masks them out (P = 0 exactly).
+  int ld_row[C::LOADS_PER_WAVE], ld_kc[C::LOADS_PER_WAVE], ld_vc[C::LOADS_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+    const int r = C::ROWS_PER_LOAD * (wave * C::LOADS_PER_WAVE + i) + lane / C::CPR;
+    ld_row[i] = r;
+    ld_kc[i] = (lane % C::CPR) ^ Swz::k(r);
+    ld_vc[i] = (lane % C::CPR) ^ Swz::v(r);
+  }
   float sreg = 0.f;
   int32_t preg = INT32_MAX;
-  const int vkg = tid % C::VGROUPS, vdc = tid / C::VGROUPS;   // V staging: 4-key group, d chunk
-  const bool v_stager = vdc < C::DC;
-
-  // Keys past the end are clamped to the last row: their loads stay in bounds and
-  // unconditional, and their position INT32_MAX masks them out (P = 0 exactly).
-  auto load_tile = [&](int t) {
+  auto issue_tile = [&](int t, int buf) {
     const int kb = t * kBN;
 #pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int p = tid + i * kAttnWaves * 64;
-      const int r = p / C::DC, c = p % C::DC;
-      const int key = min(kb + r, m - 1);
-      kreg[i] = *reinterpret_cast<const u32x4*>(k + ((int64_t)key * hkv + kvh) * D + 8 * c);
-    }
-    if (v_stager) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = min(kb + 4 * vkg + r, m - 1);
-        vreg[r] = *reinterpret_cast<const u32x4*>(v + ((int64_t)key * hkv + kvh) * D + 8 * vdc);
-      }
+    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+      const int key = min(kb + ld_row[i], m - 1);
+      const int64_t rowoff = ((int64_t)key * hkv + kvh) * D;
+      const int slot = (wave * C::LOADS_PER_WAVE + i) * 512;   // 512 bf16 = 1 KiB per wave load
+      lds_load16(k + rowoff + 8 * ld_kc[i], &k_lds[buf][slot]);
+      lds_load16(v + rowoff + 8 * ld_vc[i], &v_lds[buf][slot]);
     }
     if (tid < kBN) {
       const int key = kb + tid;
@@ -137,36 +156,20 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
       preg = key < m ? pk : INT32_MAX;
     }
   };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-      const int p = tid + i * kAttnWaves * 64;
-      const int r = p / C::DC, c = p % C::DC;
-      *reinterpret_cast<u32x4*>(&k_lds[buf][r][8 * c]) = kreg[i];
-    }
-    if (v_stager) {
-      // 4 keys x 8 d -> 8 rows of V^T, 4 keys (8 bytes) each.  Adjacent d-chunks visit
-      // the 8 rows in opposite parity order so one instruction writes both bank halves.
-      const int g4 = vkg & 3;
-      const int col = (vkg >> 2) * 16 + ((g4 == 1) ? 8 : (g4 == 2) ? 4 : (g4 == 3 ? 12 : 0));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int e2 = e ^ (vdc & 1);
-        const int d = 8 * vdc + e2;
-        const int w = e2 >> 1;
-        const uint32_t sel = (e2 & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 pk = {__builtin_amdgcn_perm(vreg[1][w], vreg[0][w], sel),
-                    __builtin_amdgcn_perm(vreg[3][w], vreg[2][w], sel)};
-        const int pchunk = (col >> 3) ^ ((d >> 1) & 7);
-        *reinterpret_cast<u32x2*>(&vt_lds[buf][d][8 * pchunk + (col & 7)]) = pk;
-      }
-    }
+  auto finish_tile = [&](int buf) {   // after the tile's loads have completed
     if (tid < kBN) {
 #pragma unroll
       for (int j = 0; j < HPW; ++j) bias_lds[buf][j][tid] = sreg * hgain[j];
       kpos_lds[buf][tid] = preg;
     }
   };
+
+  // V^T operand addressing (ds_read_b64_tr_b16): 16-lane group g = lane/16 covers
+  // d = 32u + 16(g%2) + (0..15); its lane i addresses key 16*s2 + (8r) + 4*half + i/4 and
+  // d columns 32u + 16(g%2) + 4(i%4) .. +3 (half a 16-byte chunk).
+  const int gi = lane & 15, gg = lane >> 4;
+  const int vkey_lane = 4 * half + (gi >> 2);          // key offset within a 16-key step (r = 0)
+  const int vd_lane = 16 * (gg & 1) + 4 * (gi & 3);   // d offset within a 32-wide d tile
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -175,14 +178,19 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
     for (int i = 0; i < 16; ++i) oacc[u][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f, neg_mc = 0.f;
 
-  load_tile(0);
-  store_tile(0);
+  const int rows_end = min(m, (qt + 1) * C::ROWS);
+  const int n_tiles = (rows_end + kBN - 1) / kBN;
+  issue_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  finish_tile(0);
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     const int kb = t * kBN;
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1);   // buf^1 was last read before the previous barrier
+    const uint16_t* kt_lds = k_lds[buf];
+    const uint16_t* vt_lds = v_lds[buf];
 
     if (wave_live && kb <= wave_last) {
       // S^T tile: keys kb + 32*kt + (8*g + 4*half + r) for register 4g+r, query = row.
@@ -207,7 +215,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
       for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&k_lds[buf][32 * kt + l32][16 * s + 8 * half]);
+          const int r = 32 * kt + l32;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt_lds[r * D + 8 * ((2 * s + half) ^ Swz::k(r))]);
           sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
         }
       }
@@ -264,16 +273,26 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
       }
 #pragma unroll
       for (int u = 0; u < D / 32; ++u) {
-        const int d = 32 * u + l32;
-        const int sw = (d >> 1) & 7;
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&vt_lds[buf][d][8 * ((2 * s2 + half) ^ sw)]);
-          oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[s2], oacc[u], 0, 0, 0);
+          u32x2 part[2];
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int key = 16 * s2 + 8 * r + vkey_lane;
+            const int dcol = 32 * u + vd_lane;
+            const int off = key * D + 8 * ((dcol >> 3) ^ Swz::v(key)) + (dcol & 7);
+            part[r] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(&vt_lds[off])));
+          }
+          const u32x4 a4 = {part[0][0], part[0][1], part[1][0], part[1][1]};
+          oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pf[s2], oacc[u], 0, 0, 0);
         }
       }
     }
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    if (t + 1 < n_tiles) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's share of tile t+1 has landed
+      finish_tile(buf ^ 1);
+    }
     __syncthreads();
   }
 

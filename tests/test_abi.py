@@ -28,7 +28,7 @@ def declared_functions():
 def lib():
     if not os.path.exists(LIB):
         pytest.fail("libtokengate.so is not built (python -m learned_token_pruning_scorer_amd.build)")
-    lib = ctypes.CDLL(LIB)
+    lib = ctypes.CDLL(LIB, mode=os.RTLD_NOW)   # every symbol must resolve at load time
     i32, i64, p, f32, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_size_t
     lib.tg_status_string.restype = ctypes.c_char_p
     lib.tg_status_string.argtypes = [i32]
