@@ -27,6 +27,13 @@ if ROOT not in sys.path:
 METRIC = "gated-prefill input tokens/s at 16k/128k; attn TFLOP/s and select GB/s vs peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+CALIB_BYTES = 1 << 30          # streaming copy in --profile-steps mode: reads and writes this many bytes
+# HBM bytes per launch of the attention kernel on long128k, from rocprofv3 FETCH_SIZE and WRITE_SIZE
+# scaled by the same counters' reading of the calibration copy (profiles/long128k_hbm_counters.md).
+# Reported only while the kernel source is the one the counters were taken on.
+ATTN_TRAFFIC = {"workload": "long128k", "bytes": 114899275,
+                "source": "learned_token_pruning_scorer_amd/csrc/tg_attention.hip",
+                "sha256": "8ea07288da4ac9ff416aa39ab0e62a5b6bcc6fa75ce39c591b41951dc1b69139"}
 
 
 def parse():
@@ -37,10 +44,11 @@ def parse():
     ap.add_argument("--workload", default="long128k")
     ap.add_argument("--also", default="niah16k", help="second workload reported beside the main one ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-score-rows", type=int, default=8192)
-    ap.add_argument("--cpu-attn-rows", type=int, default=256)
+    ap.add_argument("--cpu-score-rows", type=int, default=131072)
+    ap.add_argument("--cpu-attn-rows", type=int, default=8192)
     ap.add_argument("--profile-steps", type=int, default=0,
-                    help="if > 0: run only this many steps of the main workload, no JSON (for rocprofv3)")
+                    help="if > 0: run only this many steps of the main workload, then one streaming "
+                         "copy of CALIB_BYTES (the scale for HBM byte counters); no JSON (for rocprofv3)")
     return ap.parse_args()
 
 
@@ -117,6 +125,19 @@ class Path:
         return wall / steps, stage.mean(axis=0), np.median(stage, axis=0)
 
 
+def attention_traffic(workload):
+    """Counter-measured HBM bytes per attention launch, or None if stale or for another workload."""
+    import hashlib
+    if workload != ATTN_TRAFFIC["workload"]:
+        return None
+    try:
+        with open(os.path.join(ROOT, ATTN_TRAFFIC["source"]), "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return ATTN_TRAFFIC["bytes"] if digest == ATTN_TRAFFIC["sha256"] else None
+
+
 def cpu_baseline(name, score_rows, attn_rows):
     """The float64 oracle on a bounded sample of the same workload, scaled to tokens/s."""
     try:
@@ -151,15 +172,17 @@ def cpu_baseline(name, score_rows, attn_rows):
     q64, k64, v64 = (inputs.to_f64(a, w.dtype) for a in (ai.q, ai.k, ai.v))
     t = time.perf_counter()
     oracle.gated_attention(q64, k64, v64, kept, s_full[kept], ai.gain, ai.tau, rows=arows)
+    t_attn_sample = time.perf_counter() - t
     # attention cost of a row grows with the keys it sees: scale by the causal work ratio
     work_sample = float(np.sum(arows + 1))
     work_all = m * (m + 1) / 2.0
-    t_attn = (time.perf_counter() - t) * (work_all / work_sample)
+    t_attn = t_attn_sample * (work_all / work_sample)
     total = t_score + t_select + t_gather + t_attn
+    measured = t_score * (len(rows) / w.n) + t_select + t_gather + t_attn_sample
     return {"value": w.n / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"{name}: gate score on {len(rows)} of {w.n} rows, full select and gather, "
                        f"attention on {len(arows)} of {m} query rows; each scaled to the full workload "
-                       f"(score by rows, attention by causal key count)"),
+                       f"(score by rows, attention by causal key count); {measured:.1f} s of CPU time measured"),
             "stage_seconds": {"score": t_score, "select": t_select, "gather": t_gather, "attention": t_attn}}
 
 
@@ -180,6 +203,11 @@ def main():
     if args.profile_steps > 0:
         for _ in range(args.profile_steps):
             path.step()
+        torch.cuda.synchronize()
+        # a plain streaming copy of known size: its FETCH_SIZE / WRITE_SIZE give the counters' scale
+        src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
         print(f"[bench] profiled {args.profile_steps} steps of {args.workload}", file=sys.stderr, flush=True)
         return 0
@@ -227,7 +255,7 @@ def main():
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "tau": w.tau},
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel", "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": attention_traffic(w.name)},
         "cpu_baseline": cpu,
         "stages": {
             "us_mean": {"score": stage_mean[0], "select": stage_mean[1], "gather": stage_mean[2],
