@@ -154,8 +154,11 @@ tg_status tg_gather_kept(int32_t dtype, int64_t n, int32_t d_model, const void* 
  *              (bias off)
  *   tau        (host) temperature, finite and > 0
  *   out        [m, n_q_heads, head_dim] in dtype (bf16 rounded to nearest even)
- * Arithmetic (bf16): Q.K^T and P.V on bf16 MFMA with float32 accumulation, online
- * softmax in float32 (exp2), P rounded to bf16 for the P.V product.
+ * Arithmetic (bf16): Q is scaled by log2(e)/(sqrt(head_dim) tau) and rounded to bf16;
+ * Q.K^T and P.V run on bf16 MFMA with float32 accumulation; the bias enters the same
+ * accumulation with the score and gain each split into two bf16 parts (relative error
+ * below 2^-16); online softmax in float32 (exp2), P rounded to bf16 for the P.V product.
+ * q, k, v, s_kept and gain must be finite (NaN inputs give undefined output).
  * Supported: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0; q, k, v, out
  * 16-byte aligned.  m = 0 is a no-op.
  */

@@ -19,6 +19,10 @@ LIB_NAME = "libtokengate.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["tg_api.hip", "tg_score.hip", "tg_select.hip", "tg_gather.hip", "tg_attention.hip"]
 ARCH = "gfx950"
+# Per-source extra flags.  The attention kernel's inputs are finite by contract; without
+# NaN semantics the compiler does not re-canonicalise every MFMA result before taking a
+# max, which halves the vector instructions of the row max.
+EXTRA_FLAGS = {"tg_attention.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -52,7 +56,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-        _run([cc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj])
+        _run([cc, *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 
     workers = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8"))))

@@ -8,35 +8,44 @@
 // article, section "トークンゲート付きアテンションとは").  Adopted form:
 //     logit[i,j] = q_i . k_j / (sqrt(d) tau) + gain[h] s_kept[j],   pos[j] <= pos[i]
 //
-// bf16 kernel (flash attention for CDNA4, wave64):
+// bf16 kernel (flash attention for CDNA4, wave64).  On this part the softmax's vector
+// work per tile is about as long as the tile's MFMA work, and a wave issues one
+// instruction at a time, so the kernel is built to issue as few instructions per
+// tile as it can:
 //  * a workgroup = 4 waves = 32 query rows x 4 (row-block, head) slots; the heads of
 //    one workgroup share a key/value head (grouped-query attention), so each K/V
-//    tile staged in LDS serves every wave;
-//  * K and V tiles of 64 keys go from HBM straight into LDS (global_load_lds, 16
-//    bytes per lane: no staging registers, no VALU), double-buffered, with the next
-//    tile in flight while the current one is consumed.  Both keep the natural
-//    [key][d] layout with the 16-byte chunks of each row XOR-swizzled by the row,
-//    chosen so that the operand reads below are bank-conflict free;
+//    tile staged in LDS serves every wave; two workgroups share a CU;
+//  * K and V tiles of 64 keys go from HBM straight into LDS by DMA (global_load_lds,
+//    16 bytes per lane), double-buffered, issued from inline asm so that the
+//    compiler does not make later LDS reads wait for them; the global address is a
+//    scalar base advanced per tile plus per-lane offsets computed once (only the
+//    ragged last tile recomputes clamped ones);
+//  * 16-byte chunks of each K/V row are XOR-swizzled by the row so that the operand
+//    reads are bank-conflict free; every operand read is a per-lane address fixed
+//    for the whole loop plus an immediate offset (the loop is unrolled by two so
+//    the buffer index is a constant);
 //  * scores are computed transposed, S^T = K . Q^T, on v_mfma_f32_32x32x16_bf16: a
-//    lane then owns ONE query and 16 keys per 32x32 tile, so the row max / row sum
-//    are in-register plus one exchange between the two lane halves;
-//  * the key bias enters through the MFMA accumulator: S^T starts from
-//    gain[h] s_kept[j] sqrt(d) tau (the bias in q.k units, staged per tile in LDS),
-//    so S = q.k + that and the base-2 logit is S * log2(e)/(sqrt(d) tau) -- one FMA
-//    with the running max folded in gives the exponent;
-//  * lazy rescaling: the running max (and with it O and the row sum) is only moved
-//    when a tile's max exceeds it by more than 8 in the base-2 exponent, so P stays
-//    below 2^8 and most tiles skip the O rescale;
+//    lane owns ONE query and 16 keys per 32x32 tile, so row max / row sum are
+//    in-register plus one exchange between the two lane halves;
+//  * Q is pre-scaled by log2(e)/(sqrt(d) tau), and one extra 16-wide MFMA k-step per
+//    32 keys adds both the key bias and minus the running max: key rows carry
+//    [s_hi, s_hi, s_lo, s_lo, 1, 0..] (the kept score split into two bf16 parts),
+//    query columns [cG_hi, cG_lo, cG_hi, cG_lo, -m, 0..] with cG = gain[h] in base-2
+//    units.  The accumulator then holds the base-2 logit minus the running max, and
+//    P = exp2(S) needs no further vector arithmetic;
+//  * lazy rescaling: the running max (kept bf16-exact) moves only when a tile's max
+//    exceeds it by more than 8 in the base-2 exponent, so P stays below 2^8 and most
+//    tiles skip the O rescale;
 //  * P^T stays in registers as the B operand of O^T = V^T . P^T; its row sums come
 //    from v_dot2_f32_bf16 on the packed bf16 P that the MFMA consumes.  The V^T
 //    operand is read from the [key][d] tile with ds_read_b64_tr_b16: each 16-lane
-//    group addresses 4 keys x 16 d and lane L receives the 4 keys at d0 + L.  The
-//    32x32 accumulator layout leaves each lane half with keys {4h..4h+3,
-//    8+4h..8+4h+3} of every 16-key step, which is what two such reads deliver;
-//  * workgroups are numbered longest-first (the causal triangle's last query
-//    tiles first), and consecutive workgroup ids map to different key/value heads,
-//    which the dispatcher spreads round-robin over the 8 XCDs, so each XCD's L2
-//    holds the K/V of one head.
+//    group addresses 4 keys x 16 d and lane L receives the 4 keys at d0 + L;
+//  * workgroups are numbered longest-first (the causal triangle's last query tiles
+//    first), and consecutive workgroup ids map to different key/value heads, which
+//    the dispatcher spreads round-robin over the 8 XCDs, so each XCD's L2 holds the
+//    K/V of one head.
+#include <type_traits>
+
 #include "tg_common.h"
 
 namespace tg {
@@ -46,17 +55,30 @@ constexpr int kBN = 64;   // keys per tile
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) void gbl_void_t;
 
-// 16 bytes per lane from global memory straight into LDS (lane l -> lds + 16 l; the
-// LDS address must be wave-uniform).  The explicit global address-space cast is needed
-// for the host compilation pass to accept the call.
-__device__ __forceinline__ void lds_load16(const void* gptr, void* lds) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)const_cast<void*>(gptr), (lds_void_t*)lds, 16, 0, 0);
+// Global -> LDS DMA issued from inline asm: the compiler does not track these, so it
+// does not serialise later LDS reads behind them; the kernel waits for them itself
+// (wait_dma) before the barrier that publishes a tile.  M0 (the LDS destination,
+// wave-uniform) is saved and restored around the issue; the global address is a
+// 64-bit scalar base plus a 32-bit per-lane offset.
+__device__ __forceinline__ void dma16x2(uint32_t ko, const void* kb, uint32_t km0, uint32_t vo, const void* vb,
+                                        uint32_t vm0) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
+               "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %6\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "s"(km0), "v"(ko), "s"(kb), "s"(vm0), "v"(vo), "s"(vb) : "memory");
 }
+__device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t m0v) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "s"(m0v), "v"(voff), "s"(sbase) : "memory");
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-
-// XOR swizzles of the 16-byte chunks of a tile row (row = key within the tile).
+// XOR swizzles of the 16-byte chunks of a tile row (row = key within the tile).  The
+// K swizzle depends only on the row's low bits, so it is the same for rows r and r + 32
+// and a lane's K operand address is fixed for the whole loop; the V^T reads see keys
+// 4h..4h+3 (+8, +16 s2) in a lane, whose swizzle is likewise fixed per lane.
 template <int D> struct TileSwz;
 template <> struct TileSwz<128> {   // 256-byte rows: every row starts at bank 0
   static __device__ __forceinline__ int k(int r) { return r & 15; }
@@ -69,31 +91,30 @@ template <> struct TileSwz<64> {    // 128-byte rows: consecutive rows alternate
 
 template <int D, int HPW>
 struct AttnCfg {
-  static constexpr int ROWS = 32 * kAttnWaves / HPW;    // query rows per workgroup
-  static constexpr int CPR = D / 8;                      // 16-byte chunks per K/V row
-  static constexpr int ROWS_PER_LOAD = 64 / CPR;         // rows one wave-wide 1 KiB load covers
-  static constexpr int LOADS_PER_WAVE = kBN * CPR / 64 / kAttnWaves;
-  static_assert(LOADS_PER_WAVE >= 1, "tile loads");
+  static constexpr int ROWS = 32 * kAttnWaves / HPW;
+  static constexpr int CPR = D / 8;
+  static constexpr int ROWS_PER_LOAD = 64 / CPR;
+  static constexpr int LPW = kBN * CPR / 64 / kAttnWaves;   // wave loads per tile (per K or V)
+  static constexpr int TILE = kBN * D * 2;              // bytes of one K or V tile
+  // LDS layout (bytes)
+  static constexpr int K0 = 0, V0 = 2 * TILE, SB = 4 * TILE, PB = SB + 2 * kBN * 4, BYTES = PB + 2 * kBN * 4;
 };
 
-template <int D, int HPW>
+template <int D, int HPW, bool BIAS>
 __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
     int m, int hq, int hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos, const float* __restrict__ s_kept,
     const float* __restrict__ gain, float c_scale, float bias_scale, float rescale_thr,
     uint16_t* __restrict__ out, int n_qtiles) {
   using C = AttnCfg<D, HPW>;
-  using Swz = TileSwz<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) float bias_lds[2][HPW][kBN];
-  __shared__ __attribute__((aligned(16))) int32_t kpos_lds[2][kBN];
+  using S = TileSwz<D>;
+  __shared__ __attribute__((aligned(16))) char lds[C::BYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)lds;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
 
-  // workgroup -> (key/value head, head slot, query tile), longest tiles first
   const int group = hq / hkv;
   const int slots_per_kv = group / HPW;
   const int units = hkv * slots_per_kv;
@@ -101,202 +122,219 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
   const int qt = n_qtiles - 1 - blockIdx.x / units;
   const int kvh = unit / slots_per_kv;
   const int head0 = kvh * group + (unit % slots_per_kv) * HPW;
-  const int hh = wave % HPW;
-  const int head = head0 + hh;
-  const int q0 = qt * C::ROWS + (wave / HPW) * 32;   // this wave's first query row
+  const int head = head0 + wave % HPW;
+  const int q0 = qt * C::ROWS + (wave / HPW) * 32;
   const int row = q0 + l32;
   const bool wave_live = q0 < m;
-  const int wave_last = min(m - 1, q0 + 31);         // last valid row of this wave
+  const int wave_last = min(m - 1, q0 + 31);
 
-  // Q fragments: B operand of S^T, lane holds Q[row][16s + 8*half .. +7]
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    if (row < m)
-      qf[s] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)row * hq + head) * D + 16 * s + 8 * half);
-    else
+    if (row < m) {
+      const bf16x8 raw = *reinterpret_cast<const bf16x8*>(q + ((int64_t)row * hq + head) * D + 16 * s + 8 * half);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<__bf16>(static_cast<float>(raw[e]) * c_scale);
+    } else {
       qf[s] = bf16x8{};
+    }
   }
   const int32_t qpos = row < m ? (pos ? pos[row] : row) : INT32_MAX;
-  const bool use_bias = s_kept != nullptr;
-  float hgain[HPW];
-#pragma unroll
-  for (int j = 0; j < HPW; ++j) hgain[j] = use_bias ? gain[head0 + j] * bias_scale : 0.f;
-
-  // ---- tile loads: K and V global -> LDS directly; bias and positions via registers ----
-  // Wave w's load i covers tile rows ROWS_PER_LOAD*(w*LOADS_PER_WAVE + i) + lane/CPR; lane
-  // writes physical chunk lane%CPR of its row, i.e. logical chunk (lane%CPR) ^ swizzle(row).
-  // Keys past the end are clamped to the last row: the loads stay in bounds, and their
-  // position INT32_MAX masks them out (P = 0 exactly).
-  int ld_row[C::LOADS_PER_WAVE], ld_kc[C::LOADS_PER_WAVE], ld_vc[C::LOADS_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-    const int r = C::ROWS_PER_LOAD * (wave * C::LOADS_PER_WAVE + i) + lane / C::CPR;
-    ld_row[i] = r;
-    ld_kc[i] = (lane % C::CPR) ^ Swz::k(r);
-    ld_vc[i] = (lane % C::CPR) ^ Swz::v(r);
+  // extra k-step, B operand (lane half 0): [cG_hi, cG_lo, cG_hi, cG_lo, -m, 0, 0, 0] with
+  // G = gain sqrt(d) tau (so c G s = gain s in base-2 logit units) and m the running max
+  __bf16 cg_hi = static_cast<__bf16>(0.f), cg_lo = static_cast<__bf16>(0.f);
+  if (BIAS) {
+    const float cG = gain[head] * bias_scale * c_scale;
+    cg_hi = static_cast<__bf16>(cG);
+    cg_lo = static_cast<__bf16>(cG - static_cast<float>(cg_hi));
   }
-  float sreg = 0.f;
-  int32_t preg = INT32_MAX;
+  auto make_qext = [&](float mrun) {
+    bf16x8 e = bf16x8{};
+    if (half == 0) { e[0] = cg_hi; e[1] = cg_lo; e[2] = cg_hi; e[3] = cg_lo; e[4] = static_cast<__bf16>(-mrun); }
+    return e;
+  };
+
+  // ---- DMA: per-lane byte offsets relative to the tile's first key (constant across tiles) ----
+  const int64_t key_stride = (int64_t)hkv * D * 2;   // bytes between consecutive keys
+  uint32_t koff[C::LPW], voff[C::LPW], ldsk[C::LPW];
+  int lrow[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int r = C::ROWS_PER_LOAD * (wave * C::LPW + i) + lane / C::CPR;
+    lrow[i] = r;
+    koff[i] = (uint32_t)(r * key_stride) + 16 * ((lane % C::CPR) ^ S::k(r));
+    voff[i] = (uint32_t)(r * key_stride) + 16 * ((lane % C::CPR) ^ S::v(r));
+    ldsk[i] = (uint32_t)((wave * C::LPW + i) * 1024);
+  }
+  const char* kbase = reinterpret_cast<const char*>(k) + (int64_t)kvh * D * 2;
+  const char* vbase = reinterpret_cast<const char*>(v) + (int64_t)kvh * D * 2;
   auto issue_tile = [&](int t, int buf) {
     const int kb = t * kBN;
+    const char* kt_g = kbase + kb * key_stride;
+    const char* vt_g = vbase + kb * key_stride;
+    if (kb + kBN <= m) {
 #pragma unroll
-    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-      const int key = min(kb + ld_row[i], m - 1);
-      const int64_t rowoff = ((int64_t)key * hkv + kvh) * D;
-      const int slot = (wave * C::LOADS_PER_WAVE + i) * 512;   // 512 bf16 = 1 KiB per wave load
-      lds_load16(k + rowoff + 8 * ld_kc[i], &k_lds[buf][slot]);
-      lds_load16(v + rowoff + 8 * ld_vc[i], &v_lds[buf][slot]);
-    }
-    if (tid < kBN) {
-      const int key = kb + tid;
-      const int kc = min(key, m - 1);
-      sreg = use_bias ? s_kept[kc] : 0.f;
-      const int32_t pk = pos ? pos[kc] : kc;
-      preg = key < m ? pk : INT32_MAX;
-    }
-  };
-  auto finish_tile = [&](int buf) {   // after the tile's loads have completed
-    if (tid < kBN) {
+      for (int i = 0; i < C::LPW; ++i) {
+        dma16x2(koff[i], kt_g, lds0 + C::K0 + buf * C::TILE + ldsk[i], voff[i], vt_g,
+                lds0 + C::V0 + buf * C::TILE + ldsk[i]);
+      }
+    } else {   // ragged last tile: keys past the end are clamped to the last key
 #pragma unroll
-      for (int j = 0; j < HPW; ++j) bias_lds[buf][j][tid] = sreg * hgain[j];
-      kpos_lds[buf][tid] = preg;
+      for (int i = 0; i < C::LPW; ++i) {
+        const int64_t shift = (int64_t)(min(kb + lrow[i], m - 1) - (kb + lrow[i])) * key_stride;
+        dma16x2((uint32_t)(koff[i] + shift), kt_g, lds0 + C::K0 + buf * C::TILE + ldsk[i], (uint32_t)(voff[i] + shift),
+                vt_g, lds0 + C::V0 + buf * C::TILE + ldsk[i]);
+      }
+    }
+    const uint32_t soff = 4u * (uint32_t)(min(kb + lane, m - 1) - kb);
+    if (BIAS && wave == 0) dma4(soff, s_kept + kb, lds0 + C::SB + buf * kBN * 4);
+    if (wave == 1) {
+      if (pos) dma4(soff, pos + kb, lds0 + C::PB + buf * kBN * 4);
+      else reinterpret_cast<int32_t*>(lds + C::PB + buf * kBN * 4)[lane] = min(kb + lane, m - 1);
     }
   };
 
-  // V^T operand addressing (ds_read_b64_tr_b16): 16-lane group g = lane/16 covers
-  // d = 32u + 16(g%2) + (0..15); its lane i addresses key 16*s2 + (8r) + 4*half + i/4 and
-  // d columns 32u + 16(g%2) + 4(i%4) .. +3 (half a 16-byte chunk).
+  // ---- LDS operand addresses (bytes, buffer 0); other buffers/steps are immediate offsets ----
+  uint32_t ka[D / 16];   // K A-operand: row l32 (+32 kt), chunk (2s + half) ^ swz
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) ka[s] = (uint32_t)(l32 * D * 2 + 16 * ((2 * s + half) ^ S::k(l32)));
   const int gi = lane & 15, gg = lane >> 4;
-  const int vkey_lane = 4 * half + (gi >> 2);          // key offset within a 16-key step (r = 0)
-  const int vd_lane = 16 * (gg & 1) + 4 * (gi & 3);   // d offset within a 32-wide d tile
+  const int vkey_lane = 4 * half + (gi >> 2);
+  const int vd_lane = 16 * (gg & 1) + 4 * (gi & 3);
+  uint32_t va[D / 32];   // V^T operand via ds_read_b64_tr_b16: key vkey_lane (+16 s2 + 8 r), d tile u
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) {
+    const int dcol = 32 * u + vd_lane;
+    va[u] = (uint32_t)(vkey_lane * D * 2 + 2 * (8 * ((dcol >> 3) ^ S::v(vkey_lane)) + (dcol & 7)));
+  }
 
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int u = 0; u < D / 32; ++u)
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[u][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f, neg_mc = 0.f;
+  float m_run = 0.f, l_run = 0.f, l_run2 = 0.f;   // m_run: bf16-exact running max (base-2 units)
+  bf16x8 qext = make_qext(0.f);
 
   const int rows_end = min(m, (qt + 1) * C::ROWS);
   const int n_tiles = (rows_end + kBN - 1) / kBN;
-  issue_tile(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  finish_tile(0);
-  __syncthreads();
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  auto tile = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int kb = t * kBN;
-    if (t + 1 < n_tiles) issue_tile(t + 1, buf ^ 1);   // buf^1 was last read before the previous barrier
-    const uint16_t* kt_lds = k_lds[buf];
-    const uint16_t* vt_lds = v_lds[buf];
-
-    if (wave_live && kb <= wave_last) {
-      // S^T tile: keys kb + 32*kt + (8*g + 4*half + r) for register 4g+r, query = row.
-      // The accumulator starts at the key bias (q.k units), so S = q.k + bias.
-      f32x16 sacc[2];
-      if (use_bias) {
+    if (!(wave_live && kb <= wave_last)) return;
+    f32x16 sacc[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 bb = *reinterpret_cast<const f32x4*>(&bias_lds[buf][hh][32 * kt + 8 * g + 4 * half]);
+      for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[kt][4 * g + r] = bb[r];
-          }
-      } else {
+    for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+      for (int kt = 0; kt < 2; ++kt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + ka[s] + (C::K0 + buf * C::TILE + kt * 32 * D * 2));
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
       }
+    }
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const int r = 32 * kt + l32;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt_lds[r * D + 8 * ((2 * s + half) ^ Swz::k(r))]);
-          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
-        }
+    for (int kt = 0; kt < 2; ++kt) {
+      uint32_t hh = 0, ll = 0;
+      if (BIAS) {
+        const float sr = *reinterpret_cast<const float*>(lds + 4 * l32 + (C::SB + buf * kBN * 4 + kt * 128));
+        const __bf16 s_hi = static_cast<__bf16>(sr);
+        const __bf16 s_lo = static_cast<__bf16>(sr - static_cast<float>(s_hi));
+        hh = (uint32_t)__builtin_bit_cast(uint16_t, s_hi) * 0x10001u;
+        ll = (uint32_t)__builtin_bit_cast(uint16_t, s_lo) * 0x10001u;
       }
-      if ((kb + kBN - 1 > q0) || (kb + kBN > m)) {   // tile straddles the causal edge or the end
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int kk = 32 * kt + 8 * g + 4 * half;
-            typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-            const i32x4 kp = *reinterpret_cast<const i32x4*>(&kpos_lds[buf][kk]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              if (kp[r] > qpos) sacc[kt][4 * g + r] = -INFINITY;
-          }
-      }
-      float mt = sacc[0][0];
+      const u32x4 e = {half == 0 ? hh : 0u, half == 0 ? ll : 0u, half == 0 ? 0x3f80u : 0u, 0u};   // 1.0 at k = 4
+      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, e), qext, sacc[kt], 0, 0, 0);
+    }
+    if ((kb + kBN - 1 > q0) || (kb + kBN > m)) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kt][i]);
-      mt = pair_max(mt);
-      // lazy rescale: move the running max only when this tile exceeds it by > 2^8
-      if (__ballot(mt > m_run + rescale_thr)) {
-        const float m_new = fmaxf(m_run, mt);
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_scale);
-        m_run = m_new;
-        neg_mc = -m_new * c_scale;
-        l_run *= alpha;
+        for (int g = 0; g < 4; ++g) {
+          const int kk = 32 * kt + 8 * g + 4 * half;
+          typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+          const i32x4 kp = *reinterpret_cast<const i32x4*>(lds + C::PB + buf * kBN * 4 + 4 * kk);
 #pragma unroll
-        for (int u = 0; u < D / 32; ++u)
+          for (int r = 0; r < 4; ++r)
+            if (kp[r] > qpos || kb + kk + r >= m) sacc[kt][4 * g + r] = -INFINITY;
+        }
+    }
+    float mt = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[u][i] *= alpha;
+    for (int i = 2; i < 16; i += 2) mt = fmaxf(mt, fmaxf(sacc[0][i], sacc[0][i + 1]));
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(sacc[1][i], sacc[1][i + 1]));
+    mt = pair_max(mt);   // tile max of S - m (base-2 units)
+    // first tile: adopt its max; later: move the max only when exceeded by > 2^8
+    if (t == 0 || __ballot(mt > rescale_thr)) {
+      const float m_new = static_cast<float>(static_cast<__bf16>(m_run + (t == 0 ? mt : fmaxf(mt, 0.f))));
+      const float delta = m_new - m_run;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+      m_run = m_new;
+      qext = make_qext(m_run);
+      l_run *= alpha;
+      l_run2 *= alpha;
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[u][i] *= alpha;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kt][i] -= delta;
+    }
+    bf16x8 pf[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      u32x4 w;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const float p0 = __builtin_amdgcn_exp2f(sacc[s2 >> 1][8 * (s2 & 1) + 2 * e2]);
+        const float p1 = __builtin_amdgcn_exp2f(sacc[s2 >> 1][8 * (s2 & 1) + 2 * e2 + 1]);
+        const uint32_t pk = pack_bf16x2(p0, p1);
+        w[e2] = pk;
+        if (e2 & 1) l_run2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, l_run2, false);
+        else l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, l_run, false);
       }
-      // P = exp2(S c - m c), packed to bf16 as the B operand of the P.V step: step s2
-      // covers keys 16*s2 .. +15; element e of lane half h is key 16*s2 + (e < 4 ? 4h + e :
-      // 8 + 4h + e - 4) = register 8*(s2%2) + e of tile s2/2
-      bf16x8 pf[4];
-      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-      const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+      pf[s2] = __builtin_bit_cast(bf16x8, w);
+    }
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) {
-        u32x4 w;
+        u32x2 part[2];
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[s2 >> 1][8 * (s2 & 1) + 2 * e2], c_scale, neg_mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[s2 >> 1][8 * (s2 & 1) + 2 * e2 + 1], c_scale, neg_mc));
-          // (bit-cast a scalar, not the vector element: clang folds the latter to element 0)
-          const uint32_t pk = pack_bf16x2(p0, p1);
-          w[e2] = pk;
-          l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, l_run, false);
-        }
-        pf[s2] = __builtin_bit_cast(bf16x8, w);
-      }
-#pragma unroll
-      for (int u = 0; u < D / 32; ++u) {
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          u32x2 part[2];
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const int key = 16 * s2 + 8 * r + vkey_lane;
-            const int dcol = 32 * u + vd_lane;
-            const int off = key * D + 8 * ((dcol >> 3) ^ Swz::v(key)) + (dcol & 7);
-            part[r] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(&vt_lds[off])));
-          }
-          const u32x4 a4 = {part[0][0], part[0][1], part[1][0], part[1][1]};
-          oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pf[s2], oacc[u], 0, 0, 0);
-        }
+        for (int r = 0; r < 2; ++r)
+          part[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(lds + va[u] + (C::V0 + buf * C::TILE + (16 * s2 + 8 * r) * D * 2))));
+        const u32x4 a4 = {part[0][0], part[0][1], part[1][0], part[1][1]};
+        oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pf[s2], oacc[u], 0, 0, 0);
       }
     }
-    if (t + 1 < n_tiles) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's share of tile t+1 has landed
-      finish_tile(buf ^ 1);
-    }
+  };
+
+  issue_tile(0, 0);
+  wait_dma();
+  __syncthreads();
+  for (int t = 0; t < n_tiles; t += 2) {
+    if (t + 1 < n_tiles) issue_tile(t + 1, 1);
+    tile(t, std::integral_constant<int, 0>{});
+    wait_dma();
     __syncthreads();
+    if (t + 1 < n_tiles) {
+      if (t + 2 < n_tiles) issue_tile(t + 2, 0);
+      tile(t + 1, std::integral_constant<int, 1>{});
+      wait_dma();
+      __syncthreads();
+    }
   }
 
-  const float l_tot = pair_sum(l_run);   // wave-uniform exchange
+  const float l_tot = pair_sum(l_run + l_run2);
   if (row < m) {
     const float inv = 1.0f / l_tot;
     uint16_t* orow = out + ((int64_t)row * hq + head) * D;
@@ -389,10 +427,17 @@ static tg_status launch_attn_bf16(int m, int hq, int hkv, const void* q, const v
   const int n_qtiles = (m + C::ROWS - 1) / C::ROWS;
   const int64_t grid = (int64_t)n_qtiles * (hq / HPW);
   if (grid > INT32_MAX) return TG_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((attn_bf16_kernel<D, HPW>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0, st, m, hq, hkv,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, bias_scale,
-                     8.0f / c_scale, static_cast<uint16_t*>(out), n_qtiles);
+  constexpr float kRescaleThreshold = 8.0f;   // base-2 exponent headroom of P
+  if (s_kept)
+    hipLaunchKernelGGL((attn_bf16_kernel<D, HPW, true>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0, st, m, hq,
+                       hkv, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, bias_scale, kRescaleThreshold,
+                       static_cast<uint16_t*>(out), n_qtiles);
+  else
+    hipLaunchKernelGGL((attn_bf16_kernel<D, HPW, false>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0, st, m,
+                       hq, hkv, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                       static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, bias_scale, kRescaleThreshold,
+                       static_cast<uint16_t*>(out), n_qtiles);
   TG_CHECK_LAUNCH();
   return TG_OK;
 }
