@@ -36,6 +36,9 @@
 //  * lazy rescaling: the running max (kept bf16-exact) moves only when a tile's max
 //    exceeds it by more than 8 in the base-2 exponent, so P stays below 2^8 and most
 //    tiles skip the O rescale;
+//  * operand reads are issued ahead of the work that waits on them: the first two
+//    k-steps' K operands before the next tile's DMA, the first d tile's V^T
+//    operands before the softmax;
 //  * P^T stays in registers as the B operand of O^T = V^T . P^T; its row sums come
 //    from v_dot2_f32_bf16 on the packed bf16 P that the MFMA consumes.  The V^T
 //    operand is read from the [key][d] tile with ds_read_b64_tr_b16: each 16-lane
@@ -221,7 +224,12 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  auto tile = [&](int t, auto bufc) {
+  constexpr int KPRE = 2;
+  auto read_k = [&](int s, int kt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    return *reinterpret_cast<const bf16x8*>(lds + ka[s] + (C::K0 + buf * C::TILE + kt * 32 * D * 2));
+  };
+  auto tile = [&](int t, auto bufc, const bf16x8 (&kpre)[KPRE][2]) {
     constexpr int buf = decltype(bufc)::value;
     const int kb = t * kBN;
     if (!(wave_live && kb <= wave_last)) return;
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
     for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(lds + ka[s] + (C::K0 + buf * C::TILE + kt * 32 * D * 2));
+        const bf16x8 a = s < KPRE ? kpre[s < KPRE ? s : 0][kt] : read_k(s, kt, bufc);
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
       }
     }
@@ -269,6 +277,14 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
     for (int i = 2; i < 16; i += 2) mt = fmaxf(mt, fmaxf(sacc[0][i], sacc[0][i + 1]));
 #pragma unroll
     for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(sacc[1][i], sacc[1][i + 1]));
+    // V^T operands of the first d tile: read now, consumed after the softmax
+    u32x2 vpre[4][2];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+        vpre[s2][r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(lds + va[0] + (C::V0 + buf * C::TILE + (16 * s2 + 8 * r) * D * 2))));
     mt = pair_max(mt);   // tile max of S - m (base-2 units)
     // first tile: adopt its max; later: move the max only when exceeded by > 2^8
     if (t == 0 || __ballot(mt > rescale_thr)) {
@@ -304,7 +320,12 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
       pf[s2] = __builtin_bit_cast(bf16x8, w);
     }
 #pragma unroll
-    for (int u = 0; u < D / 32; ++u) {
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const u32x4 a4 = {vpre[s2][0][0], vpre[s2][0][1], vpre[s2][1][0], vpre[s2][1][1]};
+      oacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pf[s2], oacc[0], 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 1; u < D / 32; ++u) {
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) {
         u32x2 part[2];
@@ -322,13 +343,25 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
   wait_dma();
   __syncthreads();
   for (int t = 0; t < n_tiles; t += 2) {
-    if (t + 1 < n_tiles) issue_tile(t + 1, 1);
-    tile(t, std::integral_constant<int, 0>{});
+    {
+      bf16x8 kp[KPRE][2];
+#pragma unroll
+      for (int s = 0; s < KPRE; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) kp[s][kt] = read_k(s, kt, std::integral_constant<int, 0>{});
+      if (t + 1 < n_tiles) issue_tile(t + 1, 1);
+      tile(t, std::integral_constant<int, 0>{}, kp);
+    }
     wait_dma();
     __syncthreads();
     if (t + 1 < n_tiles) {
+      bf16x8 kp[KPRE][2];
+#pragma unroll
+      for (int s = 0; s < KPRE; ++s)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) kp[s][kt] = read_k(s, kt, std::integral_constant<int, 1>{});
       if (t + 2 < n_tiles) issue_tile(t + 2, 0);
-      tile(t + 1, std::integral_constant<int, 1>{});
+      tile(t + 1, std::integral_constant<int, 1>{}, kp);
       wait_dma();
       __syncthreads();
     }

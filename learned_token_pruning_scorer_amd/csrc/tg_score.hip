@@ -12,6 +12,8 @@
 // reduction over hidden units is mostly in-register.  Both operands are staged
 // through LDS in k-chunks of 64 (double-buffered); X streams from HBM once and
 // W1 (<= 1 MiB) is re-read from L2 by every workgroup.
+#include <type_traits>
+
 #include "tg_common.h"
 
 namespace tg {
@@ -246,6 +248,187 @@ static tg_status launch_score_bf16(int n, int d_model, const void* x, int64_t ld
   return TG_OK;
 }
 
+
+// ---------------------------------------------------------------------------------
+// bf16 path, d_hidden 256: the same tile (all 256 hidden units x BT tokens per
+// workgroup, C^T = W1 . X^T on 32x32x16 MFMA) fed through an NS-stage LDS ring by
+// DMA (global_load_lds, 16 bytes per lane).  A stage holds a 64-wide k-chunk: every
+// row segment is one whole 128-byte line, and up to NS - 1 chunks are in flight while
+// one is consumed.  The DMA is issued from inline asm so that the compiler does not
+// make the operand reads wait for it; the kernel waits for exactly the chunk it
+// needs (s_waitcnt vmcnt) and publishes it with one barrier per chunk.  Rows are
+// 128 bytes; their 16-byte chunks are XOR-swizzled by (row >> 1) & 7, which makes
+// the b128 operand reads bank-conflict free and keeps each lane's operand address
+// fixed for the whole loop (rows 32 i + l32 share the swizzle of l32).
+// ---------------------------------------------------------------------------------
+constexpr int kRingKC = 64;                 // k elements per stage
+constexpr int kRingRow = kRingKC * 2;       // bytes per row per stage
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ int ring_swz(int row) { return (row >> 1) & 7; }
+
+// one 1 KiB global -> LDS DMA: 64-bit scalar base + 32-bit lane offset; M0 = LDS
+// destination (wave-uniform), saved and restored around the issue
+__device__ __forceinline__ void ring_dma(uint32_t off, const void* base, uint32_t m0v) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "s"(m0v), "v"(off), "s"(base) : "memory");
+}
+
+template <int BTW, int NS>
+struct RingTile {
+  static constexpr int H = 256, AT = 4, WH = 2, WT = kScoreWaves / WH, BT = 32 * BTW * WT;
+  static constexpr int WB = H * kRingRow, XB = BT * kRingRow, STAGE = WB + XB;
+  static constexpr int WI = WB / 1024 / kScoreWaves, XI = XB / 1024 / kScoreWaves;   // DMAs per wave per stage
+  static_assert(WI >= 1 && XI >= 1, "stage split over the waves");
+};
+
+template <int BTW, int NS>
+__global__ __launch_bounds__(kScoreWaves * 64, 1) void score_ring_kernel(
+    int n, int d_model, const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w1,
+    const float* __restrict__ b1, const uint16_t* __restrict__ w2, float b2, float* __restrict__ scores) {
+  using T = RingTile<BTW, NS>;
+  constexpr int H = T::H, BT = T::BT, AT = T::AT, WT = T::WT;
+  __shared__ __attribute__((aligned(16))) char ring[NS * T::STAGE];
+  __shared__ __attribute__((aligned(16))) float w2f[H];
+  __shared__ __attribute__((aligned(16))) float b1f[H];
+  __shared__ float red[T::WH][BT];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)ring;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5, l32 = lane & 31;
+  const int wh = wave / WT, wt = wave % WT;
+  const int tok0 = blockIdx.x * BT;
+
+  for (int i = tid; i < H; i += kScoreWaves * 64) {
+    w2f[i] = bf16_to_f32(w2[i]);
+    b1f[i] = b1 ? b1[i] : 0.f;
+  }
+
+  // DMA j of this wave fills rows 8 (I wave + j) + lane/8 of the W (or X) stage; the lane
+  // writes physical chunk lane%8 of its row, which holds logical chunk (lane%8) ^ swz(row).
+  // Token rows past the end re-read the last token (their scores are never written).
+  uint32_t wo[T::WI], wm[T::WI], xo[T::XI], xm[T::XI];
+#pragma unroll
+  for (int j = 0; j < T::WI; ++j) {
+    const int r = 8 * (T::WI * wave + j) + lane / 8;
+    wo[j] = (uint32_t)((r * d_model + 8 * ((lane % 8) ^ ring_swz(r))) * 2);
+    wm[j] = (uint32_t)((T::WI * wave + j) * 1024);
+  }
+#pragma unroll
+  for (int j = 0; j < T::XI; ++j) {
+    const int r = 8 * (T::XI * wave + j) + lane / 8;
+    const int64_t rt = min(tok0 + r, n - 1) - tok0;
+    xo[j] = (uint32_t)((rt * ldx + 8 * ((lane % 8) ^ ring_swz(r))) * 2);
+    xm[j] = (uint32_t)(T::WB + (T::XI * wave + j) * 1024);
+  }
+  const char* wg = reinterpret_cast<const char*>(w1);
+  const char* xg = reinterpret_cast<const char*>(x) + (int64_t)tok0 * ldx * 2;
+  auto issue = [&](int c, int slot) {
+#pragma unroll
+    for (int j = 0; j < T::WI; ++j) ring_dma(wo[j], wg + c * kRingRow, lds0 + slot * T::STAGE + wm[j]);
+#pragma unroll
+    for (int j = 0; j < T::XI; ++j) ring_dma(xo[j], xg + c * kRingRow, lds0 + slot * T::STAGE + xm[j]);
+  };
+
+  // operand byte address of k-step ks for row l32 (plus 32-row tile offsets)
+  uint32_t oa[kRingKC / 16];
+#pragma unroll
+  for (int ks = 0; ks < kRingKC / 16; ++ks) oa[ks] = (uint32_t)(l32 * kRingRow + 16 * ((2 * ks + half) ^ ring_swz(l32)));
+
+  f32x16 acc[AT][BTW];
+#pragma unroll
+  for (int a = 0; a < AT; ++a)
+#pragma unroll
+    for (int b = 0; b < BTW; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+
+  const int nch = d_model / kRingKC;
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c)
+    if (c < nch) issue(c, c);
+
+  auto step = [&](int c, auto slotc) {
+    constexpr int slot = decltype(slotc)::value;
+    constexpr int per_chunk = T::WI + T::XI;
+    // chunk c has landed once at most min(NS - 2, nch - 1 - c) later chunks are outstanding
+    const int later = min(NS - 2, nch - 1 - c);
+    if (later >= 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NS > 3 ? 2 * per_chunk : 0) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NS > 2 ? per_chunk : 0) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // chunk c visible to all waves; chunk c - 1's slot free for reuse
+    if (c + NS - 1 < nch) issue(c + NS - 1, (slot + NS - 1) % NS);
+    const char* st = ring + slot * T::STAGE;
+#pragma unroll
+    for (int ks = 0; ks < kRingKC / 16; ++ks) {
+      bf16x8 af[AT], bfr[BTW];
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+        af[a] = *reinterpret_cast<const bf16x8*>(st + oa[ks] + 32 * kRingRow * (wh * AT + a));
+#pragma unroll
+      for (int b = 0; b < BTW; ++b)
+        bfr[b] = *reinterpret_cast<const bf16x8*>(st + T::WB + oa[ks] + 32 * kRingRow * (wt * BTW + b));
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+#pragma unroll
+        for (int b = 0; b < BTW; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+    }
+  };
+  for (int c = 0; c < nch; c += NS) {   // unrolled by NS so the stage slot is a constant
+    step(c, std::integral_constant<int, 0>{});
+    if (NS > 1 && c + 1 < nch) step(c + 1, std::integral_constant<int, 1 % NS>{});
+    if (NS > 2 && c + 2 < nch) step(c + 2, std::integral_constant<int, 2 % NS>{});
+    if (NS > 3 && c + 3 < nch) step(c + 3, std::integral_constant<int, 3 % NS>{});
+  }
+
+  // epilogue: lane holds token 32 (wt BTW + b) + l32 and hidden units
+  // 32 (wh AT + a) + 8 g + 4 half + r of tile (a, b)
+  float part[BTW];
+#pragma unroll
+  for (int b = 0; b < BTW; ++b) part[b] = 0.f;
+#pragma unroll
+  for (int a = 0; a < AT; ++a)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int hid = 32 * (wh * AT + a) + 8 * g + 4 * half;
+      const f32x4 ww = *reinterpret_cast<const f32x4*>(&w2f[hid]);
+      const f32x4 bb = *reinterpret_cast<const f32x4*>(&b1f[hid]);
+#pragma unroll
+      for (int b = 0; b < BTW; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part[b] = fmaf(ww[r], gelu_exact(acc[a][b][4 * g + r] + bb[r]), part[b]);
+    }
+#pragma unroll
+  for (int b = 0; b < BTW; ++b) {
+    part[b] += swap_halves(part[b]);
+    if (half == 0) red[wh][32 * (wt * BTW + b) + l32] = part[b];
+  }
+  __syncthreads();
+  for (int t = tid; t < BT; t += kScoreWaves * 64) {
+    if (tok0 + t < n) {
+      float s = 0.f;
+#pragma unroll
+      for (int w = 0; w < T::WH; ++w) s += red[w][t];
+      scores[tok0 + t] = s + b2;
+    }
+  }
+}
+
+template <int BTW, int NS>
+static tg_status launch_score_ring(int n, int d_model, const void* x, int64_t ldx, const void* w1, const float* b1,
+                                   const void* w2, float b2, float* scores, hipStream_t stream) {
+  constexpr int BT = RingTile<BTW, NS>::BT;
+  const int grid = (n + BT - 1) / BT;
+  hipLaunchKernelGGL((score_ring_kernel<BTW, NS>), dim3(grid), dim3(kScoreWaves * 64), 0, stream, n, d_model,
+                     static_cast<const uint16_t*>(x), ldx, static_cast<const uint16_t*>(w1), b1,
+                     static_cast<const uint16_t*>(w2), b2, scores);
+  TG_CHECK_LAUNCH();
+  return TG_OK;
+}
+
 }  // namespace tg
 
 extern "C" tg_status tg_gate_score(int32_t dtype, int64_t n, int32_t d_model, int32_t d_hidden,
@@ -269,8 +452,9 @@ extern "C" tg_status tg_gate_score(int32_t dtype, int64_t n, int32_t d_model, in
   if (d_model % kScoreKC != 0 || ldx % 8 != 0) return TG_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(w1)) & 15u) return TG_ERR_UNSUPPORTED;
   const int nn = static_cast<int>(n);
-  // d_hidden 256: 256-token tiles once there are enough of them to fill the chip (halves the
-  // L2 re-reads of W1 per token); 64/128 always use 256-token tiles (8 waves along tokens).
+  // d_hidden 256: DMA ring; 256-token tiles (two stages) once there are enough of them to
+  // fill the chip, which halves the W1 re-reads per token, else 128-token tiles (three
+  // stages).  The row offsets of one tile must fit 32 bits.  64/128: register-staged tiles.
   const bool big = n >= 65536;
   switch (d_hidden) {
     case 64:
@@ -278,8 +462,9 @@ extern "C" tg_status tg_gate_score(int32_t dtype, int64_t n, int32_t d_model, in
     case 128:
       return launch_score_bf16<128, 1>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
     case 256:
-      return big ? launch_score_bf16<256, 2>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st)
-                 : launch_score_bf16<256, 1>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
+      if ((int64_t)ldx * 2 * 256 > INT32_MAX || (int64_t)d_model * 2 * 256 > INT32_MAX) return TG_ERR_UNSUPPORTED;
+      return big ? launch_score_ring<2, 2>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st)
+                 : launch_score_ring<1, 3>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
     default:
       return TG_ERR_UNSUPPORTED;
   }
