@@ -6,6 +6,8 @@
  *   tg_select_topk      keeps every question token and the K best document tokens
  *   tg_gather_kept      compacts the kept rows (and their scores) in position order
  *   tg_gated_attention  attention over the kept tokens with the score as a key bias
+ * plus tg_select_topk_multi (several budgets in one launch) and tg_select_random (the
+ * random-K selector).
  *
  * Sources, cited by page title and section:
  *   aiproducthub.cn "斯坦福伯克利TokenGate 预填充提速11.3倍", section 事件详情
@@ -119,6 +121,34 @@ size_t tg_select_workspace_bytes(int64_t n);
 tg_status tg_select_topk(int64_t n, const float* scores, int64_t doc_begin, int64_t doc_end,
                          int64_t k, int32_t* kept_idx, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * tg_select_topk_multi -- tg_select_topk for several budgets of the same scores in one
+ * launch (one trained gate serves every budget: aiproducthub.cn, section 事件详情;
+ * aisight.pl, section "Wyniki").  Budget b's kept list (m_b = tg_num_kept(n, doc_begin,
+ * doc_end, ks[b]) ascending positions, exactly tg_select_topk's) is written at
+ * kept_idx + sum_{c < b} m_c.
+ *   ks         (host) [n_budgets] budgets, each >= 0; 1 <= n_budgets <= 8
+ *   kept_idx   [sum_b m_b] int32 output
+ * Other arguments, workspace and errors as tg_select_topk.
+ */
+tg_status tg_select_topk_multi(int64_t n, const float* scores, int64_t doc_begin, int64_t doc_end,
+                               const int64_t* ks, int32_t n_budgets, int32_t* kept_idx, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * tg_select_random -- the pages' random-K selector (aiproducthub.cn, section 事件详情;
+ * news.chathome.org, section "ベンチマーク"): every position outside the document plus a
+ * uniformly random min(k, D)-subset of the document, ascending.  Position i draws the key
+ * (uint32) of the high half of output i (counting from 0) of SplitMix64 seeded with
+ * `seed`: x_i = seed + (i + 1) * 0x9E3779B97F4A7C15 (mod 2^64), then
+ *     z = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9;  z = (z ^ (z >> 27)) * 0x94D049BB133111EB;
+ *     z ^= z >> 31;  key = z >> 32
+ * and the min(k, D) largest document keys are kept (equal keys: lower position first).
+ * Deterministic for a given seed.  Arguments, workspace and errors as tg_select_topk.
+ */
+tg_status tg_select_random(int64_t n, int64_t doc_begin, int64_t doc_end, int64_t k, uint64_t seed,
+                           int32_t* kept_idx, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * tg_gather_kept -- compaction of the kept rows: layers above the gate see only the

@@ -49,6 +49,10 @@ _lib.tg_select_workspace_bytes.restype = _sz
 _lib.tg_select_workspace_bytes.argtypes = [_i64]
 _lib.tg_select_topk.restype = _i32
 _lib.tg_select_topk.argtypes = [_i64, _p, _i64, _i64, _i64, _p, _p, _sz, _p]
+_lib.tg_select_topk_multi.restype = _i32
+_lib.tg_select_topk_multi.argtypes = [_i64, _p, _i64, _i64, ctypes.POINTER(ctypes.c_int64), _i32, _p, _p, _sz, _p]
+_lib.tg_select_random.restype = _i32
+_lib.tg_select_random.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_uint64, _p, _p, _sz, _p]
 _lib.tg_gather_kept.restype = _i32
 _lib.tg_gather_kept.argtypes = [_i32, _i64, _i32, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p]
 _lib.tg_gated_attention.restype = _i32
@@ -160,6 +164,50 @@ def tg_select_topk(scores, doc_begin: int, doc_end: int, k: int, out=None, works
     ws = workspace if workspace is not None else select_workspace(n, dev)
     _check("tg_select_topk", _lib.tg_select_topk(
         n, _ptr(scores), doc_begin, doc_end, k, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(dev, stream)))
+    return out[:m]
+
+
+def tg_select_topk_multi(scores, doc_begin: int, doc_end: int, ks, out=None, workspace=None, stream=None):
+    """tg_select_topk at each budget in ks (one launch) -> list of int32 kept-position tensors."""
+    dev = _on_gpu(scores, out, workspace)
+    if scores.dtype != torch.float32 or scores.dim() != 1 or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 vector")
+    n = scores.shape[0]
+    ks = [int(k) for k in ks]
+    ms = [tg_num_kept(n, doc_begin, doc_end, k) for k in ks]
+    if not ks or min(ms) < 0:
+        raise ValueError("invalid document span or budgets")
+    total = sum(ms)
+    if out is None:
+        out = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
+    elif out.dtype != torch.int32 or out.numel() < total or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 tensor with room for every kept list")
+    ws = workspace if workspace is not None else select_workspace(n, dev)
+    karr = (ctypes.c_int64 * len(ks))(*ks)
+    _check("tg_select_topk_multi", _lib.tg_select_topk_multi(
+        n, _ptr(scores), doc_begin, doc_end, karr, len(ks), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(dev, stream)))
+    offs = [0]
+    for m in ms:
+        offs.append(offs[-1] + m)
+    return [out[offs[b]:offs[b + 1]] for b in range(len(ks))]
+
+
+def tg_select_random(n: int, doc_begin: int, doc_end: int, k: int, seed: int, device="cuda", out=None,
+                     workspace=None, stream=None):
+    """Random-K selector: non-document positions + a seeded uniform min(k, D)-subset of the document."""
+    dev = _on_gpu(out, workspace) or torch.device(device)
+    m = tg_num_kept(n, doc_begin, doc_end, k)
+    if m < 0:
+        raise ValueError("invalid document span or budget")
+    if out is None:
+        out = torch.empty(max(m, 1), dtype=torch.int32, device=dev)
+    elif out.dtype != torch.int32 or out.numel() < m or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 tensor with room for m entries")
+    ws = workspace if workspace is not None else select_workspace(n, dev)
+    _check("tg_select_random", _lib.tg_select_random(
+        n, doc_begin, doc_end, k, seed & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(dev, stream)))
     return out[:m]
 

@@ -31,8 +31,8 @@ import numpy as np
 from scipy.special import erf as _erf
 
 __all__ = [
-    "gelu", "gate_score", "num_kept", "select_topk", "gather_kept",
-    "gated_attention", "causal_attention",
+    "gelu", "gate_score", "num_kept", "select_topk", "select_topk_multi", "splitmix64", "random_keys",
+    "select_random", "gather_kept", "gated_attention", "causal_attention",
 ]
 
 
@@ -112,6 +112,55 @@ def select_topk(scores, doc_begin, doc_end, k):
     outside = np.concatenate([np.arange(0, doc_begin, dtype=np.int64),
                               np.arange(doc_end, n, dtype=np.int64)])
     return np.sort(np.concatenate([outside, chosen]).astype(np.int64))
+
+
+# ----------------------------------------------------------------------------------------
+# (2b) several budgets over the same scores  [P1 事件详情; P2 "Wyniki"]
+# One trained gate serves every budget, so the same scores are selected at several
+# budgets: each budget's kept list is the single-budget selection at that budget.
+# ----------------------------------------------------------------------------------------
+def select_topk_multi(scores, doc_begin, doc_end, ks):
+    """[select_topk(scores, doc_begin, doc_end, k) for k in ks]."""
+    return [select_topk(scores, doc_begin, doc_end, k) for k in ks]
+
+
+# ----------------------------------------------------------------------------------------
+# (2c) random-K selector  [P1 事件详情; P4 "ベンチマーク"]
+# The pages' ablation keeps a random set of K document tokens (question kept) on the
+# same backbone.  Reading: a uniformly random min(k, D)-subset of the document, drawn
+# reproducibly from a seed -- every position gets an independent uniform 32-bit key and
+# the K largest keys are kept (equal keys: lower position first, as for scores).
+# Keys: SplitMix64 (Steele, Lea, Flood, "Fast Splittable Pseudorandom Number
+# Generators", OOPSLA 2014), the key of position i being the high 32 bits of the i-th
+# output (i = 0, 1, ...) of the generator seeded with `seed`: the state advances by the
+# golden-ratio increment 0x9E3779B97F4A7C15 before each output, and the output is the
+# state passed through the variant-13 finaliser (xor-shift 30, multiply
+# 0xBF58476D1CE4E5B9, xor-shift 27, multiply 0x94D049BB133111EB, xor-shift 31).
+# ----------------------------------------------------------------------------------------
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_MIX1 = np.uint64(0xBF58476D1CE4E5B9)
+_MIX2 = np.uint64(0x94D049BB133111EB)
+
+
+def splitmix64(seed, count):
+    """The first `count` outputs of SplitMix64 seeded with `seed` (uint64 array)."""
+    with np.errstate(over="ignore"):
+        state = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) + _GOLDEN * np.arange(1, count + 1, dtype=np.uint64)
+        z = state
+        z = (z ^ (z >> np.uint64(30))) * _MIX1
+        z = (z ^ (z >> np.uint64(27))) * _MIX2
+        return z ^ (z >> np.uint64(31))
+
+
+def random_keys(seed, n):
+    """Key of positions 0..n-1: high 32 bits of the SplitMix64 outputs (uint32)."""
+    return (splitmix64(seed, n) >> np.uint64(32)).astype(np.uint32)
+
+
+def select_random(n, doc_begin, doc_end, k, seed):
+    """Kept positions of the random-K selector (int64, ascending)."""
+    keys = random_keys(seed, n).astype(np.float64)    # exact: keys < 2^32
+    return select_topk(keys, doc_begin, doc_end, k)
 
 
 # ----------------------------------------------------------------------------------------

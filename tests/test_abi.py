@@ -40,6 +40,8 @@ def lib():
     lib.tg_select_topk.argtypes = [i64, p, i64, i64, i64, p, p, sz, p]
     lib.tg_gather_kept.argtypes = [i32, i64, i32, p, i64, p, i64, p, i64, p, p, p]
     lib.tg_gated_attention.argtypes = [i32, i64, i32, i32, i32, p, p, p, p, p, p, f32, p, p]
+    lib.tg_select_topk_multi.argtypes = [i64, p, i64, i64, ctypes.POINTER(i64), i32, p, p, sz, p]
+    lib.tg_select_random.argtypes = [i64, i64, i64, i64, ctypes.c_uint64, p, p, sz, p]
     return lib
 
 
@@ -129,3 +131,23 @@ def test_attention_validation(lib):
     assert lib.tg_gated_attention(*args(d=96)) == TG_ERR_UNSUPPORTED
     assert lib.tg_gated_attention(*args(q=ctypes.c_void_p((1 << 20) + 2))) == TG_ERR_UNSUPPORTED
     assert lib.tg_gated_attention(*args(m=0)) == TG_OK
+
+
+def test_select_multi_and_random_validation(lib):
+    ws = ctypes.c_void_p(1 << 20)
+    need = lib.tg_select_workspace_bytes(1000)
+    ks = (ctypes.c_int64 * 3)(5, 50, 500)
+    assert lib.tg_select_topk_multi(1000, FAKE, 0, 900, ks, 0, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk_multi(1000, FAKE, 0, 900, ks, 9, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk_multi(1000, FAKE, 0, 900, None, 3, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    bad = (ctypes.c_int64 * 3)(5, -1, 500)
+    assert lib.tg_select_topk_multi(1000, FAKE, 0, 900, bad, 3, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk_multi(1000, None, 0, 900, ks, 3, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_topk_multi(1000, FAKE, 0, 900, ks, 3, FAKE, ws, need - 1, None) == TG_ERR_WORKSPACE
+    zero = (ctypes.c_int64 * 2)(0, 0)
+    assert lib.tg_select_topk_multi(1000, None, 0, 1000, zero, 2, None, None, 0, None) == TG_OK
+    assert lib.tg_select_random(1000, 0, 900, -1, 7, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_random(1000, 901, 900, 5, 7, FAKE, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_random(1000, 0, 900, 5, 7, None, ws, need, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_random(1000, 0, 900, 5, 7, FAKE, ws, need - 1, None) == TG_ERR_WORKSPACE
+    assert lib.tg_select_random(1000, 0, 1000, 0, 7, None, None, 0, None) == TG_OK

@@ -58,10 +58,11 @@ def test_select_workspace_reuse_across_sizes():
         kept = binding.tg_select_topk(torch.from_numpy(s.astype(np.float32)).cuda(), 5, n - 5, k, workspace=ws)
         assert np.array_equal(kept.cpu().numpy().astype(np.int64), oracle.select_topk(s, 5, n - 5, k))
     torch.cuda.synchronize()
-    # barrier counters (bytes 0..7) and the three digit histograms (2048 + 2048 + 1024 bins)
-    # are back at zero; the barrier-timeout flag (bytes 8..11) was never raised
+    # barrier counters (bytes 0..7) and the digit histograms (2048 bins shared, then 2048 and
+    # 1024 bins for each of up to 8 budgets) are back at zero; the barrier-timeout flag
+    # (bytes 8..11) was never raised
     assert int(ws[:12].count_nonzero()) == 0
-    assert int(ws[64:64 + 4 * (2048 + 2048 + 1024)].count_nonzero()) == 0
+    assert int(ws[64:64 + 4 * (2048 + 8 * 2048 + 8 * 1024)].count_nonzero()) == 0
 
 
 # --------------------------------------------------------------------------- scorer

@@ -319,3 +319,64 @@ def test_full_budget_unbiased_pipeline_equals_causal_attention():
     q = g.normal(size=(n, 2, 4)); k = g.normal(size=(n, 1, 4)); v = g.normal(size=(n, 1, 4))
     np.testing.assert_allclose(oracle.gated_attention(q, k, v, kept, s_kept, np.zeros(2), 1.0),
                                oracle.causal_attention(q, k, v), atol=1e-14)
+
+
+# ---------------------------------------------------------------- several budgets, random-K
+def test_splitmix64_known_answers(golden_dir):
+    rows = [l for l in open(os.path.join(golden_dir, "splitmix64_seed1234567.txt")) if not l.startswith("#")]
+    expect = np.array([int(l) for l in rows], dtype=np.uint64)
+    assert np.array_equal(oracle.splitmix64(1234567, len(expect)), expect)
+
+
+def test_random_keys_are_uniform_and_independent():
+    from scipy import stats
+    keys = oracle.random_keys(99, 1 << 18)
+    # top 6 bits uniform over 64 buckets
+    counts = np.bincount(keys >> 26, minlength=64)
+    assert stats.chisquare(counts).pvalue > 1e-4
+    # every bit is balanced
+    bits = (keys[:, None] >> np.arange(32, dtype=np.uint32)) & 1
+    assert np.all(np.abs(bits.mean(axis=0) - 0.5) < 0.01)
+    # consecutive positions are uncorrelated, and another seed gives another stream
+    u = keys.astype(np.float64) / 2.0 ** 32
+    assert abs(np.corrcoef(u[:-1], u[1:])[0, 1]) < 0.01
+    assert np.mean(oracle.random_keys(100, 1 << 18) == keys) < 1e-3
+
+
+def test_select_random_is_a_uniform_subset():
+    n, db, de, k = 140, 20, 120, 10
+    counts = np.zeros(n)
+    for seed in range(600):
+        kept = oracle.select_random(n, db, de, k, seed)
+        assert len(kept) == (n - (de - db)) + k and np.all(np.diff(kept) > 0)
+        assert np.all(np.isin(np.r_[0:db, de:n], kept))
+        # the chosen document positions are those holding the k largest keys
+        keys = oracle.random_keys(seed, n)
+        doc = np.arange(db, de)
+        brute = sorted(doc, key=lambda i: (-int(keys[i]), i))[:k]
+        assert np.array_equal(np.sort(brute), kept[(kept >= db) & (kept < de)])
+        counts[kept] += 1
+    # every document position is kept with probability k / D
+    from scipy import stats
+    doc_counts = counts[db:de]
+    assert stats.chisquare(doc_counts).pvalue > 1e-4
+    assert abs(doc_counts.mean() / 600 - k / (de - db)) < 1e-12
+
+
+def test_select_random_edges():
+    assert np.array_equal(oracle.select_random(50, 10, 40, 0, 3), np.r_[0:10, 40:50])
+    assert np.array_equal(oracle.select_random(50, 10, 40, 99, 3), np.arange(50))
+    assert np.array_equal(oracle.select_random(50, 25, 25, 5, 3), np.arange(50))
+
+
+def test_select_multi_is_each_budget():
+    g = np.random.default_rng(4)
+    s = np.round(g.normal(size=3000), 1)          # many ties
+    ks = [0, 1, 17, 500, 2000, 2999, 5000]
+    lists = oracle.select_topk_multi(s, 100, 2900, ks)
+    for k, kept in zip(ks, lists):
+        doc = np.arange(100, 2900)
+        brute = sorted(doc, key=lambda i: (-s[i], i))[:min(k, 2800)]
+        assert np.array_equal(kept, np.sort(np.r_[0:100, 2900:3000, brute]))
+    for a, b in zip(lists, lists[1:]):
+        assert np.all(np.isin(a, b))
