@@ -32,7 +32,8 @@ from scipy.special import erf as _erf
 
 __all__ = [
     "gelu", "gate_score", "num_kept", "select_topk", "select_topk_multi", "splitmix64", "random_keys",
-    "select_random", "gather_kept", "gated_attention", "causal_attention",
+    "select_random", "gather_kept", "gated_attention", "causal_attention", "gated_attention_lse",
+    "gated_attention_backward",
 ]
 
 
@@ -223,3 +224,87 @@ def causal_attention(q, k, v, rows=None):
     tau = 1 and positions 0..M-1."""
     m = np.asarray(q).shape[0]
     return gated_attention(q, k, v, np.arange(m), None, None, 1.0, rows=rows)
+
+
+# ----------------------------------------------------------------------------------------
+# (5) gradient of the token-gated attention  [P1 事件详情; P2 "Jak to dziala";
+#     P4 トークンゲート付きアテンションとは]
+# Top-K is not differentiable; the score enters the attention logits as a bias
+# precisely so that the loss has a gradient path back into the scorer (and into the
+# per-head gain and the temperature).  For a loss L with dL/dout = dout, by the chain
+# rule through softmax (P = softmax of the visible logits per row):
+#     dP[i, j]   = dout_i . v_j
+#     D_i        = sum_j P[i, j] dP[i, j]        (= dout_i . out_i)
+#     dZ[i, j]   = P[i, j] (dP[i, j] - D_i)      (gradient of the logit)
+#     dq_i       = sum_j dZ[i, j] k_j / (sqrt(d) tau)
+#     dk_j      += sum_i dZ[i, j] q_i / (sqrt(d) tau)      (summed over the heads of the group)
+#     dv_j      += sum_i P[i, j] dout_i                    (summed over the heads of the group)
+#     ds_kept_j  = sum_h gain[h] sum_i dZ_h[i, j]
+#     dgain[h]   = sum_j s_kept[j] sum_i dZ_h[i, j]
+#     dtau       = -(1 / tau) sum_{h,i,j} dZ_h[i, j] q_i . k_j / (sqrt(d) tau)
+# ----------------------------------------------------------------------------------------
+def gated_attention_lse(q, k, v, pos, s_kept, gain, tau):
+    """Natural-log log-sum-exp of each row's visible logits: float64 [M, Hq]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    m, hq, d = q.shape
+    group = hq // k.shape[1]
+    use_bias = s_kept is not None and gain is not None
+    scale = 1.0 / (math.sqrt(d) * float(tau))
+    visible = pos[None, :] <= pos[:, None]
+    lse = np.empty((m, hq))
+    for h in range(hq):
+        logits = (q[:, h, :] @ k[:, h // group, :].T) * scale
+        if use_bias:
+            logits = logits + float(gain[h]) * np.asarray(s_kept, dtype=np.float64)[None, :]
+        logits = np.where(visible, logits, -np.inf)
+        mx = logits.max(axis=1, keepdims=True)
+        lse[:, h] = (mx + np.log(np.exp(logits - mx).sum(axis=1, keepdims=True)))[:, 0]
+    return lse
+
+
+def gated_attention_backward(q, k, v, pos, s_kept, gain, tau, dout):
+    """Gradients (dq, dk, dv, ds_kept, dgain, dtau) of sum(out * dout), float64.
+    ds_kept and dgain are None when the bias is off."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    use_bias = s_kept is not None and gain is not None
+    if use_bias:
+        s_kept = np.asarray(s_kept, dtype=np.float64)
+        gain = np.asarray(gain, dtype=np.float64)
+    scale = 1.0 / (math.sqrt(d) * float(tau))
+    visible = pos[None, :] <= pos[:, None]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    ds = np.zeros(m) if use_bias else None
+    dgain = np.zeros(hq) if use_bias else None
+    dtau = 0.0
+    for h in range(hq):
+        g = h // group
+        qk = q[:, h, :] @ k[:, g, :].T
+        logits = qk * scale
+        if use_bias:
+            logits = logits + gain[h] * s_kept[None, :]
+        logits = np.where(visible, logits, -np.inf)
+        mx = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - mx)
+        p /= p.sum(axis=1, keepdims=True)
+        o = p @ v[:, g, :]
+        dp = dout[:, h, :] @ v[:, g, :].T
+        dsum = np.sum(dout[:, h, :] * o, axis=1, keepdims=True)
+        dz = p * (dp - dsum)
+        dq[:, h, :] = (dz @ k[:, g, :]) * scale
+        dk[:, g, :] += (dz.T @ q[:, h, :]) * scale
+        dv[:, g, :] += p.T @ dout[:, h, :]
+        if use_bias:
+            col = dz.sum(axis=0)
+            ds += gain[h] * col
+            dgain[h] = float(np.dot(col, s_kept))
+        dtau += -float(np.sum(dz * qk)) * scale / float(tau)
+    return dq, dk, dv, ds, dgain, dtau

@@ -380,3 +380,77 @@ def test_select_multi_is_each_budget():
         assert np.array_equal(kept, np.sort(np.r_[0:100, 2900:3000, brute]))
     for a, b in zip(lists, lists[1:]):
         assert np.all(np.isin(a, b))
+
+
+# ---------------------------------------------------------------- gradient of the gated attention
+def _grad_case(seed, m=9, hq=4, hkv=2, d=8):
+    g = np.random.default_rng(seed)
+    q, k, v = (g.normal(size=(m, h, d)) for h in (hq, hkv, hkv))
+    pos = np.sort(g.choice(3 * m, size=m, replace=False))
+    s = g.normal(size=m)
+    gain = g.uniform(0.5, 1.5, size=hq)
+    dout = g.normal(size=(m, hq, d))
+    return q, k, v, pos, s, gain, 1.3, dout
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_attention_backward_matches_torch_autograd(seed):
+    q, k, v, pos, s, gain, tau, dout = _grad_case(seed)
+    m, hq, d = q.shape
+    group = hq // k.shape[1]
+    t = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+         for n, a in (("q", q), ("k", k), ("v", v), ("s", s), ("gain", gain), ("tau", np.array(tau)))}
+    kk = t["k"].repeat_interleave(group, dim=1)
+    vv = t["v"].repeat_interleave(group, dim=1)
+    logits = torch.einsum("ihd,jhd->hij", t["q"], kk) / (math.sqrt(d) * t["tau"])
+    logits = logits + t["gain"][:, None, None] * t["s"][None, None, :]
+    mask = torch.tensor(pos[None, :] <= pos[:, None])
+    logits = logits.masked_fill(~mask, float("-inf"))
+    out = torch.einsum("hij,jhd->ihd", torch.softmax(logits, dim=-1), vv)
+    (out * torch.tensor(dout)).sum().backward()
+    dq, dk, dv, ds, dgain, dtau = oracle.gated_attention_backward(q, k, v, pos, s, gain, tau, dout)
+    for mine, ref in ((dq, t["q"]), (dk, t["k"]), (dv, t["v"]), (ds, t["s"]), (dgain, t["gain"])):
+        np.testing.assert_allclose(mine, ref.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert abs(dtau - float(t["tau"].grad)) < 1e-10 * max(1.0, abs(dtau))
+
+
+def test_attention_backward_matches_finite_differences():
+    q, k, v, pos, s, gain, tau, dout = _grad_case(7, m=6, hq=2, hkv=1, d=4)
+    grads = oracle.gated_attention_backward(q, k, v, pos, s, gain, tau, dout)
+
+    def loss(q_, k_, v_, s_, gain_, tau_):
+        return float(np.sum(oracle.gated_attention(q_, k_, v_, pos, s_, gain_, tau_) * dout))
+
+    base = [q, k, v, s, gain, tau]
+    eps = 1e-6
+    for which, grad in enumerate(grads):
+        arr = np.asarray(base[which], dtype=np.float64)
+        flat = arr.reshape(-1)
+        num = np.zeros(flat.shape)
+        for idx in range(flat.size):
+            up, dn = flat.copy(), flat.copy()
+            up[idx] += eps
+            dn[idx] -= eps
+            args_u, args_d = list(base), list(base)
+            args_u[which] = up.reshape(arr.shape) if arr.ndim else float(up[0])
+            args_d[which] = dn.reshape(arr.shape) if arr.ndim else float(dn[0])
+            num[idx] = (loss(*args_u) - loss(*args_d)) / (2 * eps)
+        np.testing.assert_allclose(np.asarray(grad, dtype=np.float64).reshape(-1), num, rtol=1e-6, atol=1e-8)
+
+
+def test_attention_lse_and_bias_off_gradients():
+    q, k, v, pos, s, gain, tau, dout = _grad_case(3)
+    lse = oracle.gated_attention_lse(q, k, v, pos, s, gain, tau)
+    # lse of row 0 sees only key 0 (the smallest position)
+    d = q.shape[2]
+    first = np.argmin(pos)
+    for h in range(q.shape[1]):
+        z = q[first, h] @ k[first, h // 2] / (math.sqrt(d) * tau) + gain[h] * s[first]
+        assert abs(lse[first, h] - z) < 1e-12
+    # with the bias off the score gradients are absent and the rest matches gain = 0
+    off = oracle.gated_attention_backward(q, k, v, pos, None, None, tau, dout)
+    zero = oracle.gated_attention_backward(q, k, v, pos, s, np.zeros_like(gain), tau, dout)
+    assert off[3] is None and off[4] is None
+    for a, b in zip(off[:3], zero[:3]):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+    assert abs(off[5] - zero[5]) < 1e-12
