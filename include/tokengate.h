@@ -6,8 +6,8 @@
  *   tg_select_topk      keeps every question token and the K best document tokens
  *   tg_gather_kept      compacts the kept rows (and their scores) in position order
  *   tg_gated_attention  attention over the kept tokens with the score as a key bias
- * plus tg_select_topk_multi (several budgets in one launch) and tg_select_random (the
- * random-K selector).
+ * plus tg_select_topk_multi (several budgets in one launch), tg_select_random (the
+ * random-K selector) and tg_gated_attention_backward (the gradient of the gated attention).
  *
  * Sources, cited by page title and section:
  *   aiproducthub.cn "斯坦福伯克利TokenGate 预填充提速11.3倍", section 事件详情
@@ -196,6 +196,47 @@ tg_status tg_gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, int32_
                              int32_t head_dim, const void* q, const void* k, const void* v,
                              const int32_t* pos, const float* s_kept, const float* gain, float tau,
                              void* out, void* stream);
+
+/*
+ * tg_gated_attention_lse -- tg_gated_attention that also writes each row's natural-log
+ * log-sum-exp of its visible logits, lse [m, n_q_heads] float32 (what
+ * tg_gated_attention_backward needs).  bf16 only (TG_ERR_UNSUPPORTED for float32);
+ * otherwise as tg_gated_attention.
+ */
+tg_status tg_gated_attention_lse(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                                 int32_t head_dim, const void* q, const void* k, const void* v,
+                                 const int32_t* pos, const float* s_kept, const float* gain, float tau,
+                                 void* out, float* lse, void* stream);
+
+/*
+ * tg_gated_attention_backward -- gradient of the token-gated attention: the path by which
+ * the loss reaches the scorer through the score bias, and trains the per-head gain and
+ * the temperature (aiproducthub.cn, section 事件详情; aisight.pl, section "Jak to dziala";
+ * news.chathome.org, section "トークンゲート付きアテンションとは").  For dout = dL/dout,
+ * with P the row softmax of the visible logits, dZ = P (dout v^T - rowsum(dout * out)):
+ *     dq = dZ k / (sqrt(d) tau)        dk = dZ^T q / (sqrt(d) tau)     dv = P^T dout
+ *     ds_kept[j] = sum_h gain[h] sum_i dZ_h[i,j]    dgain[h] = sum_j s_kept[j] sum_i dZ_h[i,j]
+ *     dtau = -(1/tau) sum_{h,i,j} dZ_h[i,j] q_i.k_j / (sqrt(d) tau)
+ * (dk, dv summed over the query heads of each key/value head.)
+ *   q, k, v, pos, s_kept, gain, tau   the forward's inputs
+ *   out, lse   the forward's output and tg_gated_attention_lse's log-sum-exp
+ *   dout       [m, n_q_heads, head_dim] bf16
+ *   dq, dk, dv outputs, shaped like q, k, v, bf16 (float32 accumulation)
+ *   ds_kept [m], dgain [n_q_heads]: float32 outputs, set iff s_kept / gain are
+ *   dtau       float32 output (one value) or NULL
+ *   workspace  tg_gated_attention_backward_workspace_bytes(m, n_q_heads, n_kv_heads,
+ *              head_dim) bytes, 256-byte aligned, no initial contents needed
+ * Deterministic (fixed-order reductions, no float atomics).  Supported: bf16, head_dim in
+ * {64, 128}, 16-byte aligned tensors; pos strictly increasing as for the forward.
+ */
+size_t tg_gated_attention_backward_workspace_bytes(int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                                                   int32_t head_dim);
+tg_status tg_gated_attention_backward(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, const void* q, const void* k, const void* v,
+                                      const int32_t* pos, const float* s_kept, const float* gain, float tau,
+                                      const void* out, const float* lse, const void* dout, void* dq, void* dk,
+                                      void* dv, float* ds_kept, float* dgain, float* dtau, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -58,6 +58,14 @@ _lib.tg_gather_kept.argtypes = [_i32, _i64, _i32, _p, _i64, _p, _i64, _p, _i64, 
 _lib.tg_gated_attention.restype = _i32
 _lib.tg_gated_attention.argtypes = [_i32, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _f32, _p, _p]
 
+_lib.tg_gated_attention_lse.restype = _i32
+_lib.tg_gated_attention_lse.argtypes = [_i32, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p]
+_lib.tg_gated_attention_backward_workspace_bytes.restype = _sz
+_lib.tg_gated_attention_backward_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32]
+_lib.tg_gated_attention_backward.restype = _i32
+_lib.tg_gated_attention_backward.argtypes = [_i32, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p,
+                                             _p, _p, _p, _p, _p, _p, _p, _sz, _p]
+
 lib = _lib   # raw ctypes handle (the C ABI itself)
 
 
@@ -236,9 +244,7 @@ def tg_gather_kept(x, kept_idx, scores=None, out=None, s_out=None, stream=None):
     return out[:m], (s_out[:m] if scores is not None else None)
 
 
-def tg_gated_attention(q, k, v, pos=None, s_kept=None, gain=None, tau: float = 1.0, out=None, stream=None):
-    """Token-gated causal attention; q [m, Hq, d], k/v [m, Hkv, d] -> [m, Hq, d]."""
-    dev = _on_gpu(q, k, v, pos, s_kept, gain, out)
+def _check_attention_args(q, k, v, pos, s_kept, gain):
     for t in (q, k, v):
         if t.dim() != 3 or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous [m, heads, head_dim]")
@@ -257,6 +263,14 @@ def tg_gated_attention(q, k, v, pos=None, s_kept=None, gain=None, tau: float = 1
             raise ValueError("s_kept must be contiguous float32 [m]")
         if gain.dtype != torch.float32 or gain.shape != (hq,) or not gain.is_contiguous():
             raise ValueError("gain must be contiguous float32 [Hq]")
+
+
+def tg_gated_attention(q, k, v, pos=None, s_kept=None, gain=None, tau: float = 1.0, out=None, stream=None):
+    """Token-gated causal attention; q [m, Hq, d], k/v [m, Hkv, d] -> [m, Hq, d]."""
+    dev = _on_gpu(q, k, v, pos, s_kept, gain, out)
+    _check_attention_args(q, k, v, pos, s_kept, gain)
+    m, hq, d = q.shape
+    hkv = k.shape[1]
     if out is None:
         out = torch.empty_like(q)
     _check("tg_gated_attention", _lib.tg_gated_attention(
@@ -284,3 +298,43 @@ def to_host_bits(t: torch.Tensor):
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def tg_gated_attention_lse(q, k, v, pos=None, s_kept=None, gain=None, tau: float = 1.0, out=None, lse=None,
+                           stream=None):
+    """tg_gated_attention that also returns the row log-sum-exp -> (out, lse [m, Hq] float32)."""
+    dev = _on_gpu(q, k, v, pos, s_kept, gain, out, lse)
+    _check_attention_args(q, k, v, pos, s_kept, gain)
+    m, hq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(m, hq, dtype=torch.float32, device=dev)
+    _check("tg_gated_attention_lse", _lib.tg_gated_attention_lse(
+        _dtype_code(q), m, hq, k.shape[1], d, _ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(s_kept), _ptr(gain),
+        float(tau), _ptr(out), _ptr(lse), _stream(dev, stream)))
+    return out, lse
+
+
+def tg_gated_attention_backward(q, k, v, pos, s_kept, gain, tau, out, lse, dout, workspace=None, stream=None):
+    """Gradients (dq, dk, dv, ds_kept or None, dgain or None, dtau) of sum(out * dout)."""
+    dev = _on_gpu(q, k, v, pos, s_kept, gain, out, lse, dout, workspace)
+    _check_attention_args(q, k, v, pos, s_kept, gain)
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    for t in (out, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError("out and dout must be shaped and typed like q, contiguous")
+    if lse.shape != (m, hq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be float32 [m, Hq]")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ds = torch.empty(m, dtype=torch.float32, device=dev) if s_kept is not None else None
+    dg = torch.empty(hq, dtype=torch.float32, device=dev) if gain is not None else None
+    dtau = torch.empty(1, dtype=torch.float32, device=dev)
+    need = int(_lib.tg_gated_attention_backward_workspace_bytes(m, hq, hkv, d))
+    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check("tg_gated_attention_backward", _lib.tg_gated_attention_backward(
+        _dtype_code(q), m, hq, hkv, d, _ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(s_kept), _ptr(gain), float(tau),
+        _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ds), _ptr(dg), _ptr(dtau), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(dev, stream)))
+    return dq, dk, dv, ds, dg, dtau

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
     int m, int hq, int hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos, const float* __restrict__ s_kept,
     const float* __restrict__ gain, float c_scale, float bias_scale, float rescale_thr,
-    uint16_t* __restrict__ out, int n_qtiles) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int n_qtiles) {
   using C = AttnCfg<D, HPW>;
   using S = TileSwz<D>;
   __shared__ __attribute__((aligned(16))) char lds[C::BYTES];
@@ -370,6 +370,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
   const float l_tot = pair_sum(l_run + l_run2);
   if (row < m) {
     const float inv = 1.0f / l_tot;
+    // natural-log log-sum-exp of the row's logits: (m + log2(l)) in base-2 units, times ln 2
+    if (lse && half == 0) lse[(int64_t)row * hq + head] = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
     uint16_t* orow = out + ((int64_t)row * hq + head) * D;
 #pragma unroll
     for (int u = 0; u < D / 32; ++u)
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(int m, int hq, int h
 template <int D, int HPW>
 static tg_status launch_attn_bf16(int m, int hq, int hkv, const void* q, const void* k, const void* v,
                                   const int32_t* pos, const float* s_kept, const float* gain, float c_scale,
-                                  float bias_scale, void* out, hipStream_t st) {
+                                  float bias_scale, void* out, float* lse, hipStream_t st) {
   using C = AttnCfg<D, HPW>;
   const int n_qtiles = (m + C::ROWS - 1) / C::ROWS;
   const int64_t grid = (int64_t)n_qtiles * (hq / HPW);
@@ -465,12 +467,12 @@ static tg_status launch_attn_bf16(int m, int hq, int hkv, const void* q, const v
     hipLaunchKernelGGL((attn_bf16_kernel<D, HPW, true>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0, st, m, hq,
                        hkv, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, bias_scale, kRescaleThreshold,
-                       static_cast<uint16_t*>(out), n_qtiles);
+                       static_cast<uint16_t*>(out), lse, n_qtiles);
   else
     hipLaunchKernelGGL((attn_bf16_kernel<D, HPW, false>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0, st, m,
                        hq, hkv, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, bias_scale, kRescaleThreshold,
-                       static_cast<uint16_t*>(out), n_qtiles);
+                       static_cast<uint16_t*>(out), lse, n_qtiles);
   TG_CHECK_LAUNCH();
   return TG_OK;
 }
@@ -478,28 +480,30 @@ static tg_status launch_attn_bf16(int m, int hq, int hkv, const void* q, const v
 template <int D>
 static tg_status dispatch_attn_bf16(int m, int hq, int hkv, const void* q, const void* k, const void* v,
                                     const int32_t* pos, const float* s_kept, const float* gain, float c_scale,
-                                    float bias_scale, void* out, hipStream_t st) {
+                                    float bias_scale, void* out, float* lse, hipStream_t st) {
   const int group = hq / hkv;
   if (group % 4 == 0)
-    return launch_attn_bf16<D, 4>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, st);
+    return launch_attn_bf16<D, 4>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, lse, st);
   if (group % 2 == 0)
-    return launch_attn_bf16<D, 2>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, st);
-  return launch_attn_bf16<D, 1>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, st);
+    return launch_attn_bf16<D, 2>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, lse, st);
+  return launch_attn_bf16<D, 1>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, lse, st);
 }
 
 }  // namespace tg
 
-extern "C" tg_status tg_gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
-                                        int32_t head_dim, const void* q, const void* k, const void* v,
-                                        const int32_t* pos, const float* s_kept, const float* gain, float tau,
-                                        void* out, void* stream) {
-  using namespace tg;
+namespace tg {
+
+static tg_status gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                 const void* q, const void* k, const void* v, const int32_t* pos,
+                                 const float* s_kept, const float* gain, float tau, void* out, float* lse,
+                                 void* stream) {
   if (dtype != TG_F32 && dtype != TG_BF16) return TG_ERR_INVALID_ARG;
   if (m < 0 || m > INT32_MAX || n_q_heads <= 0 || n_kv_heads <= 0) return TG_ERR_INVALID_ARG;
   if (n_q_heads % n_kv_heads != 0) return TG_ERR_INVALID_ARG;
   if ((s_kept == nullptr) != (gain == nullptr)) return TG_ERR_INVALID_ARG;
   if (!std::isfinite(tau) || !(tau > 0.f)) return TG_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return TG_ERR_UNSUPPORTED;
+  if (lse && dtype != TG_BF16) return TG_ERR_UNSUPPORTED;
   if (m == 0) return TG_OK;
   if (!q || !k || !v || !out) return TG_ERR_INVALID_ARG;
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
@@ -512,9 +516,9 @@ extern "C" tg_status tg_gated_attention(int32_t dtype, int64_t m, int32_t n_q_he
   if (dtype == TG_BF16) {
     return head_dim == 128
                ? dispatch_attn_bf16<128>(mm, n_q_heads, n_kv_heads, q, k, v, pos, s_kept, gain, c_scale,
-                                         bias_scale, out, st)
+                                         bias_scale, out, lse, st)
                : dispatch_attn_bf16<64>(mm, n_q_heads, n_kv_heads, q, k, v, pos, s_kept, gain, c_scale,
-                                        bias_scale, out, st);
+                                        bias_scale, out, lse, st);
   }
   const dim3 grid((mm + kF32Rows - 1) / kF32Rows, n_q_heads);
   if (head_dim == 128)
@@ -527,4 +531,23 @@ extern "C" tg_status tg_gated_attention(int32_t dtype, int64_t m, int32_t n_q_he
                        pos, s_kept, gain, c_scale, static_cast<float*>(out));
   TG_CHECK_LAUNCH();
   return TG_OK;
+}
+
+}  // namespace tg
+
+extern "C" tg_status tg_gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                                        int32_t head_dim, const void* q, const void* k, const void* v,
+                                        const int32_t* pos, const float* s_kept, const float* gain, float tau,
+                                        void* out, void* stream) {
+  return tg::gated_attention(dtype, m, n_q_heads, n_kv_heads, head_dim, q, k, v, pos, s_kept, gain, tau, out,
+                             nullptr, stream);
+}
+
+extern "C" tg_status tg_gated_attention_lse(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                                            int32_t head_dim, const void* q, const void* k, const void* v,
+                                            const int32_t* pos, const float* s_kept, const float* gain, float tau,
+                                            void* out, float* lse, void* stream) {
+  if (!lse && m > 0) return TG_ERR_INVALID_ARG;
+  return tg::gated_attention(dtype, m, n_q_heads, n_kv_heads, head_dim, q, k, v, pos, s_kept, gain, tau, out, lse,
+                             stream);
 }

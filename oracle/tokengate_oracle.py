@@ -264,9 +264,15 @@ def gated_attention_lse(q, k, v, pos, s_kept, gain, tau):
     return lse
 
 
-def gated_attention_backward(q, k, v, pos, s_kept, gain, tau, dout):
+def gated_attention_backward(q, k, v, pos, s_kept, gain, tau, dout, magnitudes=False):
     """Gradients (dq, dk, dv, ds_kept, dgain, dtau) of sum(out * dout), float64.
-    ds_kept and dgain are None when the bias is off."""
+    ds_kept and dgain are None when the bias is off.
+
+    With magnitudes=True a seventh item is returned: {"dgain": [Hq], "dtau": float},
+    the same sums taken over absolute values of their terms (sum_j |s_j col_j| per
+    head, and sum |dZ q.k| scale / tau).  dgain and dtau are sums with heavy
+    cancellation (each row of dZ sums to zero), so these are the scales against
+    which a rounding error in them is judged."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -285,6 +291,8 @@ def gated_attention_backward(q, k, v, pos, s_kept, gain, tau, dout):
     ds = np.zeros(m) if use_bias else None
     dgain = np.zeros(hq) if use_bias else None
     dtau = 0.0
+    mag_gain = np.zeros(hq)
+    mag_tau = 0.0
     for h in range(hq):
         g = h // group
         qk = q[:, h, :] @ k[:, g, :].T
@@ -306,5 +314,9 @@ def gated_attention_backward(q, k, v, pos, s_kept, gain, tau, dout):
             col = dz.sum(axis=0)
             ds += gain[h] * col
             dgain[h] = float(np.dot(col, s_kept))
+            mag_gain[h] = float(np.dot(np.abs(col), np.abs(s_kept)))
         dtau += -float(np.sum(dz * qk)) * scale / float(tau)
+        mag_tau += float(np.sum(np.abs(dz * qk))) * scale / float(tau)
+    if magnitudes:
+        return dq, dk, dv, ds, dgain, dtau, {"dgain": mag_gain, "dtau": mag_tau}
     return dq, dk, dv, ds, dgain, dtau

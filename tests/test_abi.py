@@ -42,6 +42,11 @@ def lib():
     lib.tg_gated_attention.argtypes = [i32, i64, i32, i32, i32, p, p, p, p, p, p, f32, p, p]
     lib.tg_select_topk_multi.argtypes = [i64, p, i64, i64, ctypes.POINTER(i64), i32, p, p, sz, p]
     lib.tg_select_random.argtypes = [i64, i64, i64, i64, ctypes.c_uint64, p, p, sz, p]
+    lib.tg_gated_attention_lse.argtypes = [i32, i64, i32, i32, i32, p, p, p, p, p, p, f32, p, p, p]
+    lib.tg_gated_attention_backward_workspace_bytes.restype = sz
+    lib.tg_gated_attention_backward_workspace_bytes.argtypes = [i64, i32, i32, i32]
+    lib.tg_gated_attention_backward.argtypes = [i32, i64, i32, i32, i32, p, p, p, p, p, p, f32, p, p, p,
+                                                p, p, p, p, p, p, p, sz, p]
     return lib
 
 
@@ -151,3 +156,38 @@ def test_select_multi_and_random_validation(lib):
     assert lib.tg_select_random(1000, 0, 900, 5, 7, None, ws, need, None) == TG_ERR_INVALID_ARG
     assert lib.tg_select_random(1000, 0, 900, 5, 7, FAKE, ws, need - 1, None) == TG_ERR_WORKSPACE
     assert lib.tg_select_random(1000, 0, 1000, 0, 7, None, None, 0, None) == TG_OK
+
+
+def test_attention_lse_and_backward_validation(lib):
+    f = ctypes.c_float
+    fwd = lambda **kw: [kw.get("dt", 1), kw.get("m", 64), 4, 2, kw.get("d", 64), FAKE, FAKE, FAKE, None, None, None,
+                        f(1.0), FAKE, kw.get("lse", FAKE), None]
+    assert lib.tg_gated_attention_lse(*fwd(lse=None)) == TG_ERR_INVALID_ARG
+    assert lib.tg_gated_attention_lse(*fwd(dt=0)) == TG_ERR_UNSUPPORTED     # float32 has no lse output
+    assert lib.tg_gated_attention_lse(*fwd(m=0, lse=None)) == TG_OK
+
+    need = lib.tg_gated_attention_backward_workspace_bytes(1000, 8, 2, 128)
+    assert need >= 1000 * 8 * 4 + 1000 * 2 * 4 and need % 256 == 0
+    assert lib.tg_gated_attention_backward_workspace_bytes(-1, 8, 2, 128) == 0
+    assert lib.tg_gated_attention_backward_workspace_bytes(2000, 8, 2, 128) > need
+    ws = ctypes.c_void_p(1 << 20)
+
+    def bwd(**kw):
+        bias = kw.get("bias", True)
+        return lib.tg_gated_attention_backward(
+            kw.get("dt", 1), kw.get("m", 1000), kw.get("hq", 8), kw.get("hkv", 2), kw.get("d", 128),
+            FAKE, FAKE, FAKE, None, FAKE if bias else None, FAKE if bias else None, f(kw.get("tau", 1.0)),
+            FAKE, FAKE, FAKE, kw.get("dq", FAKE), FAKE, FAKE, kw.get("ds", FAKE if bias else None),
+            kw.get("dg", FAKE if bias else None), None, kw.get("ws", ws), kw.get("wsb", need), None)
+
+    assert bwd(hq=6, hkv=4) == TG_ERR_INVALID_ARG
+    assert bwd(tau=-1.0) == TG_ERR_INVALID_ARG
+    assert bwd(ds=None) == TG_ERR_INVALID_ARG                 # bias on needs its gradient outputs
+    assert bwd(bias=False, dg=FAKE) == TG_ERR_INVALID_ARG
+    assert bwd(dq=None) == TG_ERR_INVALID_ARG
+    assert bwd(ws=ctypes.c_void_p((1 << 20) + 64)) == TG_ERR_INVALID_ARG
+    assert bwd(wsb=need - 1) == TG_ERR_WORKSPACE
+    assert bwd(dt=0) == TG_ERR_UNSUPPORTED
+    assert bwd(d=96) == TG_ERR_UNSUPPORTED
+    assert bwd(dq=ctypes.c_void_p((1 << 20) + 4)) == TG_ERR_UNSUPPORTED
+    assert bwd(m=0) == TG_OK

@@ -1,0 +1,141 @@
+"""Gradient of the token-gated attention on the GPU against the float64 oracle.
+
+The backward path is the one by which a loss reaches the gate through the score
+bias and trains the per-head gain and the temperature (aiproducthub.cn, section
+事件详情; aisight.pl, section "Jak to dziala").  The oracle's gradient is pinned
+on the CPU against torch autograd and finite differences.
+
+Tolerances (bf16 operands, float32 accumulation, bf16 dq/dk/dv):
+  dq, dk, dv, ds_kept   max-abs <= 3e-2 max|ref| + 1e-5, mean-abs <= 1e-2 mean|ref| + 1e-6
+  dgain[h], dtau        |err| <= 2e-2 of the same sum over absolute terms, + 1e-4
+Three roundings bound each gradient term: the scaled logit operand in bf16 (a
+relative 2^-9 per element, about 0.3% on P at unit-scale logits), P and dZ packed
+to bf16 as MFMA operands (2^-9) and the bf16 result (2^-9): about 0.8% at worst,
+hence 1e-2 on the mean; 3e-2 of the largest value leaves room for the worst
+element.  dgain and dtau are sums whose terms cancel (each row of dZ sums to zero),
+so their error is judged against the sum of the terms' magnitudes, not against the
+(possibly tiny) result; the absolute floors cover float32 rounding of results that
+are exactly zero (a single visible key gives dZ = 0).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from learned_token_pruning_scorer_amd import inputs
+from gpu_common import host_f64, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # m, hq, hkv, d, bias, gapped positions
+    (1, 4, 2, 64, True, False),
+    (37, 4, 4, 64, True, True),
+    (100, 8, 2, 128, True, False),
+    (257, 8, 1, 64, False, True),
+    (333, 16, 8, 128, True, True),
+    (600, 6, 3, 64, True, False),
+    (1088, 16, 8, 128, True, False),   # the 16k needle workload's kept rows (1024 + 64 question)
+    (4224, 16, 8, 128, True, False),   # the 32k multi-document workload's kept rows (4096 + 128)
+]
+
+
+def _case_inputs(m, hq, hkv, d, gapped, seed):
+    g = np.random.default_rng(seed)
+    bf = lambda shape: inputs.f32_to_bf16_bits(g.normal(size=shape).astype(np.float32))
+    q, k, v, dout = bf((m, hq, d)), bf((m, hkv, d)), bf((m, hkv, d)), bf((m, hq, d))
+    pos = (np.sort(g.choice(5 * m + 3, m, replace=False)) if gapped else np.arange(m)).astype(np.int32)
+    s = (g.normal(size=m) * 2).astype(np.float32)
+    gain = g.uniform(0.5, 1.5, size=hq).astype(np.float32)
+    return q, k, v, dout, pos, s, gain
+
+
+def _run(binding, q, k, v, dout, pos, s, gain, tau, bias):
+    import torch
+    dev = "cuda"
+    qt, kt, vt, dot = (binding.to_device(a, "bf16", dev) for a in (q, k, v, dout))
+    pt = torch.from_numpy(pos).to(dev)
+    st = torch.from_numpy(s).to(dev) if bias else None
+    gt = torch.from_numpy(gain).to(dev) if bias else None
+    out, lse = binding.tg_gated_attention_lse(qt, kt, vt, pt, st, gt, tau)
+    grads = binding.tg_gated_attention_backward(qt, kt, vt, pt, st, gt, tau, out, lse, dot)
+    torch.cuda.synchronize()
+    return out, lse, grads
+
+
+def _check_tensor(name, got, ref):
+    err = np.abs(got - ref)
+    scale_max, scale_mean = np.abs(ref).max(), np.abs(ref).mean()
+    log(f"  {name}: max_abs={err.max():.3e} (|ref| max {scale_max:.3e}) mean_abs={err.mean():.3e} "
+        f"(|ref| mean {scale_mean:.3e})")
+    assert np.all(np.isfinite(got)), name
+    assert err.max() <= 3e-2 * scale_max + 1e-5, name
+    assert err.mean() <= 1e-2 * scale_mean + 1e-6, name
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_matches_oracle(case):
+    binding = require_gpu()
+    m, hq, hkv, d, bias, gapped = case
+    tau = 1.1
+    q, k, v, dout, pos, s, gain = _case_inputs(m, hq, hkv, d, gapped, seed=m * 13 + hq + d)
+    log(f"[attention backward] m={m} hq={hq} hkv={hkv} d={d} bias={bias} gapped={gapped}")
+    out, lse, (dq, dk, dv, ds, dg, dtau) = _run(binding, q, k, v, dout, pos, s, gain, tau, bias)
+    f64 = lambda a: inputs.to_f64(a, "bf16")
+    ref = oracle.gated_attention_backward(f64(q), f64(k), f64(v), pos, s if bias else None,
+                                          gain if bias else None, tau, f64(dout), magnitudes=True)
+    rdq, rdk, rdv, rds, rdg, rdtau, mag = ref
+    _check_tensor("dq", host_f64(dq), rdq)
+    _check_tensor("dk", host_f64(dk), rdk)
+    _check_tensor("dv", host_f64(dv), rdv)
+    if bias:
+        _check_tensor("ds_kept", host_f64(ds), rds)
+        eg = np.abs(host_f64(dg) - rdg)
+        log(f"  dgain: max_err/magnitude={np.max(eg / np.maximum(mag['dgain'], 1e-30)):.3e}")
+        assert np.all(eg <= 2e-2 * mag["dgain"] + 1e-4)
+    else:
+        assert ds is None and dg is None
+    et = abs(float(host_f64(dtau)[0]) - rdtau)
+    log(f"  dtau: got {float(host_f64(dtau)[0]):.6e} ref {rdtau:.6e} magnitude {mag['dtau']:.3e}")
+    assert et <= 2e-2 * mag["dtau"] + 1e-4
+
+    rlse = oracle.gated_attention_lse(f64(q), f64(k), f64(v), pos, s if bias else None, gain if bias else None, tau)
+    lerr = np.abs(host_f64(lse) - rlse)
+    log(f"  lse: max_abs={lerr.max():.3e}")
+    assert lerr.max() <= 2e-2
+
+
+def test_lse_variant_leaves_the_output_unchanged():
+    """tg_gated_attention_lse writes the same output bits as tg_gated_attention."""
+    binding = require_gpu()
+    import torch
+    m, hq, hkv, d = 700, 8, 4, 128
+    q, k, v, _, pos, s, gain = _case_inputs(m, hq, hkv, d, True, seed=5)
+    qt, kt, vt = (binding.to_device(a, "bf16") for a in (q, k, v))
+    pt, st, gt = (torch.from_numpy(a).cuda() for a in (pos, s, gain))
+    o1 = binding.tg_gated_attention(qt, kt, vt, pt, st, gt, 0.8)
+    o2, _ = binding.tg_gated_attention_lse(qt, kt, vt, pt, st, gt, 0.8)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_backward_is_deterministic():
+    """Fixed-order reductions: two calls give the same bits."""
+    binding = require_gpu()
+    import torch
+    m, hq, hkv, d = 1500, 16, 8, 128
+    q, k, v, dout, pos, s, gain = _case_inputs(m, hq, hkv, d, False, seed=9)
+    _, _, g1 = _run(binding, q, k, v, dout, pos, s, gain, 1.3, True)
+    _, _, g2 = _run(binding, q, k, v, dout, pos, s, gain, 1.3, True)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_backward_zero_upstream_gradient():
+    """dout = 0 gives exactly zero gradients everywhere."""
+    binding = require_gpu()
+    import torch
+    m, hq, hkv, d = 300, 8, 2, 64
+    q, k, v, dout, pos, s, gain = _case_inputs(m, hq, hkv, d, False, seed=3)
+    _, _, grads = _run(binding, q, k, v, np.zeros_like(dout), pos, s, gain, 1.0, True)
+    for t in grads:
+        assert torch.count_nonzero(t.float()) == 0
