@@ -33,7 +33,7 @@ from scipy.special import erf as _erf
 __all__ = [
     "gelu", "gate_score", "num_kept", "select_topk", "select_topk_multi", "splitmix64", "random_keys",
     "select_random", "gather_kept", "gated_attention", "causal_attention", "gated_attention_lse",
-    "gated_attention_backward",
+    "gated_attention_backward", "rope_inv_freq", "rope", "qkv_rope", "emit_kv",
 ]
 
 
@@ -320,3 +320,63 @@ def gated_attention_backward(q, k, v, pos, s_kept, gain, tau, dout, magnitudes=F
     if magnitudes:
         return dq, dk, dv, ds, dgain, dtau, {"dgain": mag_gain, "dtau": mag_tau}
     return dq, dk, dv, ds, dgain, dtau
+
+
+# ----------------------------------------------------------------------------------------
+# (6) kept-row projection and KV emission  [P1 事件详情; P2 "Jak to dziala"; P4 仕組み]
+# Layers above the gate run on the kept tokens only, and pruned tokens get no KV
+# entries.  The step after the gather: project the kept hidden states to Q, K, V,
+# rotate Q and K by their ORIGINAL positions, and write K, V (and the positions)
+# into a cache that holds the kept tokens only, compacted.
+# Readings (the pages are silent on all of these): one fused weight W_qkv
+# [(Hq + 2 Hkv) d, d_model] (rows: the Hq query heads, then the Hkv key heads, then
+# the Hkv value heads; optional bias); rotary embedding in the rotate-half form,
+# feature i paired with i + d/2 and turned by the angle pos * theta^(-2 i / d); no
+# per-head normalisation before the rotation.
+# ----------------------------------------------------------------------------------------
+def rope_inv_freq(head_dim, theta):
+    """theta^(-2 i / d) for i = 0 .. d/2 - 1, float64."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(float(theta), -2.0 * i / head_dim)
+
+
+def rope(x, pos, theta):
+    """Rotate-half rotary embedding of x [M, H, d] at positions pos [M], float64:
+    out[:, :, i] = x_i cos a - x_{i+d/2} sin a,  out[:, :, i+d/2] = x_{i+d/2} cos a + x_i sin a,
+    a = pos * theta^(-2 i / d)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * rope_inv_freq(d, theta)[None, :]   # [M, d/2]
+    c, s = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    lo, hi = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
+
+
+def qkv_rope(x_kept, w_qkv, b_qkv, n_q_heads, n_kv_heads, head_dim, pos, theta):
+    """(q [M, Hq, d], k [M, Hkv, d], v [M, Hkv, d]) float64 from the kept rows
+    x_kept [M, d_model]: C = x_kept W_qkv^T (+ b_qkv), split by heads, rotary on q and k."""
+    x = np.asarray(x_kept, dtype=np.float64)
+    w = np.asarray(w_qkv, dtype=np.float64)
+    c = x @ w.T
+    if b_qkv is not None:
+        c = c + np.asarray(b_qkv, dtype=np.float64)[None, :]
+    m = x.shape[0]
+    nq, nk = n_q_heads * head_dim, n_kv_heads * head_dim
+    q = c[:, :nq].reshape(m, n_q_heads, head_dim)
+    k = c[:, nq:nq + nk].reshape(m, n_kv_heads, head_dim)
+    v = c[:, nq + nk:nq + 2 * nk].reshape(m, n_kv_heads, head_dim)
+    return rope(q, pos, theta), rope(k, pos, theta), v
+
+
+def emit_kv(k_cache, v_cache, pos_cache, slot0, k, v, pos):
+    """Copies of the caches with rows slot0 .. slot0 + M - 1 holding the kept tokens'
+    k, v and positions; every other row unchanged (pos_cache may be None)."""
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    m = len(k)
+    kc[slot0:slot0 + m] = k
+    vc[slot0:slot0 + m] = v
+    pc = None
+    if pos_cache is not None:
+        pc = np.array(pos_cache, copy=True)
+        pc[slot0:slot0 + m] = pos
+    return kc, vc, pc

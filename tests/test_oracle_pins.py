@@ -454,3 +454,86 @@ def test_attention_lse_and_bias_off_gradients():
     for a, b in zip(off[:3], zero[:3]):
         np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
     assert abs(off[5] - zero[5]) < 1e-12
+
+
+# --------------------------------------------------------------------------- projection, rotary, KV emission
+def test_rope_inv_freq_known_values():
+    """theta^(-2i/d) at sizes where it is a power of ten, and its constant ratio."""
+    np.testing.assert_allclose(oracle.rope_inv_freq(8, 10000.0), [1.0, 0.1, 0.01, 0.001], rtol=1e-15)
+    np.testing.assert_allclose(oracle.rope_inv_freq(4, 1e6), [1.0, 1e-3], rtol=1e-15)
+    f = oracle.rope_inv_freq(128, 1e6)
+    assert f[0] == 1.0 and len(f) == 64
+    np.testing.assert_allclose(f[1:] / f[:-1], np.full(63, 1e6 ** (-2.0 / 128)), rtol=1e-13)
+
+
+def test_rope_is_complex_multiplication():
+    """Pairs (i, i + d/2) as complex numbers z_i are multiplied by exp(1j * pos * theta_i)."""
+    g = np.random.default_rng(3)
+    m, h, d, theta = 40, 3, 16, 5000.0
+    x = g.normal(size=(m, h, d))
+    pos = g.integers(0, 200000, size=m)
+    z = x[..., : d // 2] + 1j * x[..., d // 2:]
+    freq = np.exp(-np.arange(d // 2) * (2.0 / d) * np.log(theta))
+    zr = z * np.exp(1j * pos[:, None, None] * freq[None, None, :])
+    want = np.concatenate([zr.real, zr.imag], axis=-1)
+    np.testing.assert_allclose(oracle.rope(x, pos, theta), want, rtol=1e-9, atol=1e-9)
+
+
+def test_rope_group_and_relative_position_properties():
+    g = np.random.default_rng(4)
+    m, d, theta = 30, 32, 1e6
+    x = g.normal(size=(m, 2, d))
+    p1 = g.integers(0, 5000, size=m)
+    p2 = g.integers(0, 5000, size=m)
+    # identity at position 0, composition adds positions, each pair keeps its length
+    np.testing.assert_array_equal(oracle.rope(x, np.zeros(m), theta), x)
+    np.testing.assert_allclose(oracle.rope(oracle.rope(x, p1, theta), p2, theta), oracle.rope(x, p1 + p2, theta),
+                               atol=1e-9)
+    r = oracle.rope(x, p1, theta)
+    np.testing.assert_allclose(r[..., :d // 2] ** 2 + r[..., d // 2:] ** 2, x[..., :d // 2] ** 2 + x[..., d // 2:] ** 2,
+                               rtol=1e-12)
+    # the rotated q.k depends on the positions only through their difference
+    q, k = x[:, 0:1, :], x[:, 1:2, :]
+    shift = 777
+    a = np.sum(oracle.rope(q, p1, theta) * oracle.rope(k, p2, theta), axis=-1)
+    b = np.sum(oracle.rope(q, p1 + shift, theta) * oracle.rope(k, p2 + shift, theta), axis=-1)
+    np.testing.assert_allclose(a, b, atol=1e-9)
+    # swapping the halves' roles (a transposed pairing) breaks the property above
+    bad = np.concatenate([x[..., d // 2:], x[..., :d // 2]], axis=-1)
+    assert not np.allclose(oracle.rope(bad, p1, theta), oracle.rope(x, p1, theta))
+
+
+def test_qkv_projection_matches_torch_linear():
+    """At position 0 the rotation is the identity: q, k, v are slices of a torch Linear."""
+    g = np.random.default_rng(5)
+    m, d_model, hq, hkv, d = 20, 48, 4, 2, 8
+    x = g.normal(size=(m, d_model))
+    w = g.normal(size=((hq + 2 * hkv) * d, d_model))
+    b = g.normal(size=(hq + 2 * hkv) * d)
+    lin = torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b)).numpy()
+    q, k, v = oracle.qkv_rope(x, w, b, hq, hkv, d, np.zeros(m), 1e4)
+    np.testing.assert_allclose(q.reshape(m, -1), lin[:, : hq * d], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(k.reshape(m, -1), lin[:, hq * d:(hq + hkv) * d], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(v.reshape(m, -1), lin[:, (hq + hkv) * d:], rtol=1e-12, atol=1e-12)
+    # at other positions q and k are rotated, v is not
+    pos = g.integers(0, 100000, size=m)
+    q2, k2, v2 = oracle.qkv_rope(x, w, None, hq, hkv, d, pos, 1e4)
+    q0, k0, v0 = oracle.qkv_rope(x, w, None, hq, hkv, d, np.zeros(m), 1e4)
+    np.testing.assert_allclose(q2, oracle.rope(q0, pos, 1e4), atol=1e-10)
+    np.testing.assert_allclose(k2, oracle.rope(k0, pos, 1e4), atol=1e-10)
+    np.testing.assert_array_equal(v2, v0)
+
+
+def test_emit_kv_writes_only_its_slots():
+    g = np.random.default_rng(6)
+    cap, hkv, d, m, slot0 = 50, 2, 4, 7, 20
+    kc, vc, pc = g.normal(size=(cap, hkv, d)), g.normal(size=(cap, hkv, d)), g.integers(0, 9, size=cap)
+    k, v, pos = g.normal(size=(m, hkv, d)), g.normal(size=(m, hkv, d)), np.arange(m) * 3
+    kc2, vc2, pc2 = oracle.emit_kv(kc, vc, pc, slot0, k, v, pos)
+    keep = np.r_[0:slot0, slot0 + m:cap]
+    np.testing.assert_array_equal(kc2[keep], kc[keep])
+    np.testing.assert_array_equal(vc2[keep], vc[keep])
+    np.testing.assert_array_equal(pc2[keep], pc[keep])
+    np.testing.assert_array_equal(kc2[slot0:slot0 + m], k)
+    np.testing.assert_array_equal(vc2[slot0:slot0 + m], v)
+    np.testing.assert_array_equal(pc2[slot0:slot0 + m], pos)
