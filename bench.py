@@ -46,9 +46,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-score-rows", type=int, default=131072)
     ap.add_argument("--cpu-attn-rows", type=int, default=8192)
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the timings of the attention backward and the multi-budget / random selectors")
     ap.add_argument("--profile-steps", type=int, default=0,
-                    help="if > 0: run only this many steps of the main workload, then one streaming "
-                         "copy of CALIB_BYTES (the scale for HBM byte counters); no JSON (for rocprofv3)")
+                    help="if > 0: run only this many steps of the main workload (and as many calls of "
+                         "each row timed by --no-next's rows), then one streaming copy of CALIB_BYTES "
+                         "(the scale for HBM byte counters); no JSON (for rocprofv3)")
     return ap.parse_args()
 
 
@@ -138,6 +141,58 @@ def attention_traffic(workload):
     return ATTN_TRAFFIC["bytes"] if digest == ATTN_TRAFFIC["sha256"] else None
 
 
+def _event_time_us(torch, fn, reps, warmup=3):
+    """Mean time of fn() from HIP events on the current stream (the stream the bindings launch on)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+
+
+def next_rows(path, reps):
+    """Timings of the rows beyond the forward step, on the main workload's tensors:
+    the attention backward, several budgets in one select, and the random-K selector."""
+    torch, b, w = path.torch, path.b, path.w
+    res = {}
+    # attention backward: algorithmic flops = five causal products (S, dP, dQ, dK, dV) of the
+    # forward's per-product size; the kernels recompute S and dP once more for dQ
+    g = torch.Generator(device="cuda").manual_seed(1)
+    dout = torch.randn(path.q.shape, generator=g, device="cuda", dtype=torch.float32).to(path.q.dtype)
+    out, lse = b.tg_gated_attention_lse(path.q, path.kk, path.v, path.kept, path.sk, path.gain, path.tau)
+    ws = torch.empty(max(256, int(b.lib.tg_gated_attention_backward_workspace_bytes(
+        path.m, w.n_q_heads, w.n_kv_heads, w.head_dim))), dtype=torch.uint8, device="cuda")
+    us = _event_time_us(torch, lambda: b.tg_gated_attention_backward(
+        path.q, path.kk, path.v, path.kept, path.sk, path.gain, path.tau, out, lse, dout, workspace=ws), reps)
+    flops = 2.5 * algorithmic(w, path.k)["attn_flops"]
+    res["attention_backward"] = {"us": us, "tflops": flops / (us * 1e-6) / 1e12,
+                                 "frac_mfma_peak": flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                                 "flops": flops, "note": "five causal products of size 2 M^2 d Hq / 2"}
+    us_fwd = _event_time_us(torch, lambda: b.tg_gated_attention_lse(
+        path.q, path.kk, path.v, path.kept, path.sk, path.gain, path.tau, out=out, lse=lse), reps)
+    res["attention_forward_with_lse"] = {"us": us_fwd}
+    # several budgets over one histogram of the same scores
+    ks = [path.k // 8, path.k // 4, path.k // 2, path.k]
+    outs = torch.empty(sum(w.n_kept(k) for k in ks), dtype=torch.int32, device="cuda")
+    us = _event_time_us(torch, lambda: b.tg_select_topk_multi(path.scores, w.doc_begin, w.doc_end, ks, out=outs,
+                                                               workspace=path.ws), reps)
+    byts = w.n * 4 + sum(w.n_kept(k) for k in ks) * 4
+    res["select_topk_multi"] = {"budgets": ks, "us": us, "gbs": byts / (us * 1e-6) / 1e9,
+                                "frac_hbm_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "bytes": byts}
+    kept_r = torch.empty(path.m, dtype=torch.int32, device="cuda")
+    us = _event_time_us(torch, lambda: b.tg_select_random(w.n, w.doc_begin, w.doc_end, path.k, 12345,
+                                                          out=kept_r, workspace=path.ws), reps)
+    res["select_random"] = {"k": path.k, "us": us, "gbs": path.m * 4 / (us * 1e-6) / 1e9, "bytes": path.m * 4}
+    del dout, out, lse, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(name, score_rows, attn_rows):
     """The float64 oracle on a bounded sample of the same workload, scaled to tokens/s."""
     try:
@@ -204,6 +259,8 @@ def main():
         for _ in range(args.profile_steps):
             path.step()
         torch.cuda.synchronize()
+        if not args.no_next:
+            next_rows(path, args.profile_steps)
         # a plain streaming copy of known size: its FETCH_SIZE / WRITE_SIZE give the counters' scale
         src = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -231,6 +288,11 @@ def main():
                 "stage_us_mean": {"score": st2[0], "select": st2[1], "gather": st2[2], "attention": st2[3]}}
         del p2
         torch.cuda.empty_cache()
+
+    nxt = None
+    if not args.no_next:
+        print("[bench] timing the backward and the selector variants", file=sys.stderr, flush=True)
+        nxt = next_rows(path, max(5, args.steps // 2))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -267,6 +329,7 @@ def main():
             "score_gbs": score_gbs, "score_frac_hbm_peak": score_gbs / PEAK_HBM_GBS, "score_tflops": score_tflops,
         },
         "also": also,
+        "next_rows": nxt,
     }
     print(json.dumps(out))
     return 0

@@ -386,30 +386,46 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
 // ---------------------------------------------------------------------------------
 // fixed-order sums of the partials
 // ---------------------------------------------------------------------------------
+// Blocks 0 .. ceil(m/256)-1 sum ds over the key/value heads; the last block sums dgain
+// (one wave per head) and dtau (the whole block).  Each sum's order is fixed by the
+// launch shape alone, so results are bitwise reproducible.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(int m, int hq, int hkv, int n_kblocks, int n_dkv_blocks,
                                                           const float* __restrict__ ds_part,
                                                           const float* __restrict__ dgain_part,
                                                           const float* __restrict__ dtau_part, float dtau_scale,
                                                           float* __restrict__ ds, float* __restrict__ dgain,
                                                           float* __restrict__ dtau) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (ds && j < m) {
-    float acc = 0.f;
-    for (int g = 0; g < hkv; ++g) acc += ds_part[(int64_t)g * m + j];
-    ds[j] = acc;
-  }
-  if (blockIdx.x == 0) {
-    if (dgain)
-      for (int h = threadIdx.x; h < hq; h += 256) {
-        float acc = 0.f;
-        for (int i = 0; i < n_kblocks * kDkvWaves; ++i) acc += dgain_part[(int64_t)h * n_kblocks * kDkvWaves + i];
-        dgain[h] = acc;
-      }
-    if (dtau && threadIdx.x == 0) {
+  __shared__ float red[256];
+  const int n_ds_blocks = (m + 255) / 256;
+  if ((int)blockIdx.x < n_ds_blocks) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (ds && j < m) {
       float acc = 0.f;
-      for (int i = 0; i < n_dkv_blocks * kDkvWaves; ++i) acc += dtau_part[i];
-      *dtau = acc * dtau_scale;
+      for (int g = 0; g < hkv; ++g) acc += ds_part[(int64_t)g * m + j];
+      ds[j] = acc;
     }
+    return;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int per_head = n_kblocks * kDkvWaves;
+  if (dgain)
+    for (int h = wave; h < hq; h += 4) {
+      float acc = 0.f;
+      for (int i = lane; i < per_head; i += 64) acc += dgain_part[(int64_t)h * per_head + i];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+      if (lane == 0) dgain[h] = acc;
+    }
+  if (dtau) {
+    float acc = 0.f;
+    for (int i = threadIdx.x; i < n_dkv_blocks * kDkvWaves; i += 256) acc += dtau_part[i];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+      if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) *dtau = red[0] * dtau_scale;
   }
 }
 
@@ -472,7 +488,7 @@ static tg_status attention_backward(int m, int hq, int hkv, const void* q, const
                      static_cast<uint16_t*>(dv), ds_part, dgain_part, dtau_part, n_kblocks);
   // dtau = -(1/tau) sum dZ . (q.k / (sqrt(d) tau)); the kernel summed dZ . (c2 q.k)
   const float dtau_scale = static_cast<float>(-kLn2 / (double)tau);
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((m + 255) / 256), dim3(256), 0, st, m, hq, hkv, n_kblocks, n_dkv,
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((m + 255) / 256 + 1), dim3(256), 0, st, m, hq, hkv, n_kblocks, n_dkv,
                      ds_part, dgain_part, dtau_part, dtau_scale, ds, dgain, dtau);
   TG_CHECK_LAUNCH();
   return TG_OK;
