@@ -184,6 +184,21 @@ def next_rows(path, reps):
     byts = w.n * 4 + sum(w.n_kept(k) for k in ks) * 4
     res["select_topk_multi"] = {"budgets": ks, "us": us, "gbs": byts / (us * 1e-6) / 1e9,
                                 "frac_hbm_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, "bytes": byts}
+    # kept-row projection + rotary + KV emission: 2 M d_model (Hq + 2 Hkv) d flops
+    from learned_token_pruning_scorer_amd import inputs
+    wq = b.to_device(inputs.qkv_weights(w), w.dtype, "cuda")
+    qo = torch.empty_like(path.q)
+    kc, vc = torch.empty_like(path.kk), torch.empty_like(path.v)
+    pc = torch.empty(path.m, dtype=torch.int32, device="cuda")
+    qws = torch.empty(max(256, int(b.lib.tg_qkv_rope_workspace_bytes(path.m, w.head_dim))), dtype=torch.uint8,
+                      device="cuda")
+    us = _event_time_us(torch, lambda: b.tg_qkv_rope(path.xk, wq, path.kept, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                                                     inputs.ROPE_THETA, q_out=qo, k_cache=kc, v_cache=vc,
+                                                     pos_cache=pc, workspace=qws), reps)
+    flops = 2.0 * path.m * w.d_model * (w.n_q_heads + 2 * w.n_kv_heads) * w.head_dim
+    res["qkv_rope"] = {"us": us, "tflops": flops / (us * 1e-6) / 1e12,
+                       "frac_mfma_peak": flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, "flops": flops}
+    del wq, qo, kc, vc, pc, qws
     kept_r = torch.empty(path.m, dtype=torch.int32, device="cuda")
     us = _event_time_us(torch, lambda: b.tg_select_random(w.n, w.doc_begin, w.doc_end, path.k, 12345,
                                                           out=kept_r, workspace=path.ws), reps)

@@ -7,7 +7,8 @@
  *   tg_gather_kept      compacts the kept rows (and their scores) in position order
  *   tg_gated_attention  attention over the kept tokens with the score as a key bias
  * plus tg_select_topk_multi (several budgets in one launch), tg_select_random (the
- * random-K selector) and tg_gated_attention_backward (the gradient of the gated attention).
+ * random-K selector), tg_gated_attention_backward (the gradient of the gated attention)
+ * and tg_qkv_rope (kept-row projection, rotary embedding and KV emission).
  *
  * Sources, cited by page title and section:
  *   aiproducthub.cn "斯坦福伯克利TokenGate 预填充提速11.3倍", section 事件详情
@@ -237,6 +238,36 @@ tg_status tg_gated_attention_backward(int32_t dtype, int64_t m, int32_t n_q_head
                                       const void* out, const float* lse, const void* dout, void* dq, void* dk,
                                       void* dv, float* ds_kept, float* dgain, float* dtau, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/*
+ * tg_qkv_rope -- the step after the gather: project the kept rows to queries, keys and
+ * values, rotate queries and keys by each kept token's ORIGINAL position, and write the
+ * keys, values and positions into a KV cache that holds kept tokens only (layers above
+ * the gate see only kept tokens and pruned tokens create no KV entries: aiproducthub.cn,
+ * section 事件详情; aisight.pl, section "Jak to dziala").
+ *     C = x_kept W_qkv^T (+ b_qkv)     W_qkv [(Hq + 2 Hkv) d, d_model]: rows of the Hq query
+ *                                      heads, then the Hkv key heads, then the Hkv value heads
+ *     rotary (rotate-half): for i < d/2, a = pos[j] * theta^(-2i/d),
+ *         y_i = c_i cos a - c_{i+d/2} sin a,   y_{i+d/2} = c_{i+d/2} cos a + c_i sin a
+ *     q_out[j, h, :]            = rotated query head h of row j
+ *     k_cache[slot0 + j, h, :]  = rotated key head h;  v_cache[slot0 + j, h, :] = value head h
+ *     pos_cache[slot0 + j]      = pos[j]   (if pos_cache is not NULL)
+ *   x_kept   [m, ldx] bf16 (the gathered rows)     w_qkv, b_qkv (float32 or NULL) as above
+ *   pos      [m] int32, the kept tokens' original positions (tg_select_topk's kept_idx)
+ *   q_out    [m, Hq, d] bf16;  k_cache, v_cache [cache_capacity, Hkv, d] bf16; rows outside
+ *            slot0 .. slot0 + m - 1 are not touched
+ *   workspace  tg_qkv_rope_workspace_bytes(m, d) bytes, 256-byte aligned (the rotation table)
+ * The angle is formed and reduced modulo 2 pi in float64, so positions up to 2^31 keep
+ * full float32 accuracy in cos / sin.  Supported: bf16, d in {64, 128}, (Hq + 2 Hkv) d a
+ * multiple of 128, d_model a multiple of 64, ldx a multiple of 8, 16-byte aligned
+ * tensors; rope_theta > 1.  cache_slot0 + m <= cache_capacity, else TG_ERR_INVALID_ARG.
+ */
+size_t tg_qkv_rope_workspace_bytes(int64_t m, int32_t head_dim);
+tg_status tg_qkv_rope(int32_t dtype, int64_t m, int32_t d_model, const void* x_kept, int64_t ldx,
+                      const void* w_qkv, const float* b_qkv, int32_t n_q_heads, int32_t n_kv_heads,
+                      int32_t head_dim, const int32_t* pos, float rope_theta, void* q_out, void* k_cache,
+                      void* v_cache, int32_t* pos_cache, int64_t cache_slot0, int64_t cache_capacity,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

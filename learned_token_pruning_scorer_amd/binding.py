@@ -66,6 +66,12 @@ _lib.tg_gated_attention_backward.restype = _i32
 _lib.tg_gated_attention_backward.argtypes = [_i32, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p,
                                              _p, _p, _p, _p, _p, _p, _p, _sz, _p]
 
+_lib.tg_qkv_rope_workspace_bytes.restype = _sz
+_lib.tg_qkv_rope_workspace_bytes.argtypes = [_i64, _i32]
+_lib.tg_qkv_rope.restype = _i32
+_lib.tg_qkv_rope.argtypes = [_i32, _i64, _i32, _p, _i64, _p, _p, _i32, _i32, _i32, _p, _f32, _p, _p, _p, _p, _i64,
+                             _i64, _p, _sz, _p]
+
 lib = _lib   # raw ctypes handle (the C ABI itself)
 
 
@@ -338,3 +344,44 @@ def tg_gated_attention_backward(q, k, v, pos, s_kept, gain, tau, out, lse, dout,
         _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ds), _ptr(dg), _ptr(dtau), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(dev, stream)))
     return dq, dk, dv, ds, dg, dtau
+
+
+def tg_qkv_rope(x_kept, w_qkv, pos, n_q_heads: int, n_kv_heads: int, head_dim: int, rope_theta: float,
+                b_qkv=None, q_out=None, k_cache=None, v_cache=None, pos_cache=None, cache_slot0: int = 0,
+                workspace=None, stream=None):
+    """Kept-row QKV projection + rotary embedding at original positions + KV emission.
+
+    Returns (q_out [m, Hq, d], k_cache, v_cache, pos_cache); caches default to [slot0 + m, Hkv, d]."""
+    dev = _on_gpu(x_kept, w_qkv, pos, b_qkv, q_out, k_cache, v_cache, pos_cache, workspace)
+    if x_kept.dim() != 2 or x_kept.stride(1) != 1:
+        raise ValueError("x_kept must be [m, d_model] with unit column stride")
+    m, d_model = x_kept.shape
+    n_feat = (n_q_heads + 2 * n_kv_heads) * head_dim
+    if w_qkv.shape != (n_feat, d_model) or not w_qkv.is_contiguous() or w_qkv.dtype != x_kept.dtype:
+        raise ValueError("w_qkv must be contiguous [(Hq + 2 Hkv) d, d_model] of x_kept's dtype")
+    if pos.dtype != torch.int32 or pos.shape != (m,) or not pos.is_contiguous():
+        raise ValueError("pos must be contiguous int32 [m]")
+    if b_qkv is not None and (b_qkv.dtype != torch.float32 or b_qkv.shape != (n_feat,) or not b_qkv.is_contiguous()):
+        raise ValueError("b_qkv must be contiguous float32 [(Hq + 2 Hkv) d]")
+    if q_out is None:
+        q_out = torch.empty(m, n_q_heads, head_dim, dtype=x_kept.dtype, device=dev)
+    cap = cache_slot0 + m
+    if k_cache is None:
+        k_cache = torch.empty(cap, n_kv_heads, head_dim, dtype=x_kept.dtype, device=dev)
+    if v_cache is None:
+        v_cache = torch.empty(k_cache.shape, dtype=x_kept.dtype, device=dev)
+    if (k_cache.shape != v_cache.shape or k_cache.dim() != 3 or k_cache.shape[1:] != (n_kv_heads, head_dim)
+            or not (k_cache.is_contiguous() and v_cache.is_contiguous())):
+        raise ValueError("k_cache / v_cache must be contiguous [capacity, Hkv, d]")
+    if q_out.shape != (m, n_q_heads, head_dim) or not q_out.is_contiguous():
+        raise ValueError("q_out must be contiguous [m, Hq, d]")
+    if pos_cache is not None and (pos_cache.dtype != torch.int32 or pos_cache.shape != (k_cache.shape[0],)):
+        raise ValueError("pos_cache must be int32 [capacity]")
+    need = int(_lib.tg_qkv_rope_workspace_bytes(m, head_dim))
+    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check("tg_qkv_rope", _lib.tg_qkv_rope(
+        _dtype_code(x_kept), m, d_model, _ptr(x_kept), x_kept.stride(0), _ptr(w_qkv), _ptr(b_qkv), n_q_heads,
+        n_kv_heads, head_dim, _ptr(pos), float(rope_theta), _ptr(q_out), _ptr(k_cache), _ptr(v_cache),
+        _ptr(pos_cache), cache_slot0, k_cache.shape[0], _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(dev, stream)))
+    return q_out, k_cache, v_cache, pos_cache

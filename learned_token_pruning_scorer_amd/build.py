@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 LIB_NAME = "libtokengate.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["tg_api.hip", "tg_score.hip", "tg_select.hip", "tg_gather.hip", "tg_attention.hip",
-           "tg_attention_bwd.hip"]
+           "tg_attention_bwd.hip", "tg_qkv.hip"]
 ARCH = "gfx950"
 # Per-source extra flags.  The attention kernel's inputs are finite by contract; without
 # NaN semantics the compiler does not re-canonicalise every MFMA result before taking a

@@ -56,7 +56,6 @@ namespace tg {
 constexpr int kAttnWaves = 4;
 constexpr int kBN = 64;   // keys per tile
 
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 // Global -> LDS DMA issued from inline asm: the compiler does not track these, so it

@@ -70,6 +70,26 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// LDS byte address of a __shared__ object
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)p;
+}
+
+// One 1 KiB global -> LDS DMA (global_load_lds_dwordx4): lane L reads 16 bytes at
+// base + off and writes them at LDS byte m0v + 16 L.  base is a 64-bit scalar (wave-
+// uniform) pointer, off a 32-bit per-lane byte offset, m0v the wave-uniform LDS
+// destination; M0 is saved and restored around the issue.  Issued from inline asm so
+// that the compiler does not make later LDS reads wait for it: the caller waits with
+// s_waitcnt vmcnt and publishes the data with a barrier.
+__device__ __forceinline__ void dma_lds16(uint32_t off, const void* base, uint32_t m0v) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "s"(m0v), "v"(off), "s"(base) : "memory");
+}
+
 }  // namespace tg
 
 #define TG_CHECK_LAUNCH()                                   \

@@ -263,17 +263,7 @@ static tg_status launch_score_bf16(int n, int d_model, const void* x, int64_t ld
 // ---------------------------------------------------------------------------------
 constexpr int kRingKC = 64;                 // k elements per stage
 constexpr int kRingRow = kRingKC * 2;       // bytes per row per stage
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 __device__ __forceinline__ int ring_swz(int row) { return (row >> 1) & 7; }
-
-// one 1 KiB global -> LDS DMA: 64-bit scalar base + 32-bit lane offset; M0 = LDS
-// destination (wave-uniform), saved and restored around the issue
-__device__ __forceinline__ void ring_dma(uint32_t off, const void* base, uint32_t m0v) {
-  uint32_t save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
-               : "=&s"(save) : "s"(m0v), "v"(off), "s"(base) : "memory");
-}
 
 template <int BTW, int NS>
 struct RingTile {
@@ -327,9 +317,9 @@ __global__ __launch_bounds__(kScoreWaves * 64, 1) void score_ring_kernel(
   const char* xg = reinterpret_cast<const char*>(x) + (int64_t)tok0 * ldx * 2;
   auto issue = [&](int c, int slot) {
 #pragma unroll
-    for (int j = 0; j < T::WI; ++j) ring_dma(wo[j], wg + c * kRingRow, lds0 + slot * T::STAGE + wm[j]);
+    for (int j = 0; j < T::WI; ++j) dma_lds16(wo[j], wg + c * kRingRow, lds0 + slot * T::STAGE + wm[j]);
 #pragma unroll
-    for (int j = 0; j < T::XI; ++j) ring_dma(xo[j], xg + c * kRingRow, lds0 + slot * T::STAGE + xm[j]);
+    for (int j = 0; j < T::XI; ++j) dma_lds16(xo[j], xg + c * kRingRow, lds0 + slot * T::STAGE + xm[j]);
   };
 
   // operand byte address of k-step ks for row l32 (plus 32-row tile offsets)

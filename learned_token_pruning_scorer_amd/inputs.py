@@ -30,6 +30,8 @@ from .configs import Workload
 
 STREAM_X, STREAM_W1, STREAM_W2, STREAM_SPANS = 0, 1, 3, 4
 STREAM_Q, STREAM_K, STREAM_V, STREAM_GAIN, STREAM_ROWS = 5, 6, 7, 8, 9
+STREAM_WQKV = 10
+ROPE_THETA = 1.0e6     # rotary base of the Qwen3 family whose shapes the workloads borrow
 
 _CHUNK_ROWS = 4096   # rows drawn per call; fixed so that streams are reproducible
 
@@ -192,3 +194,14 @@ def sample_rows(m: int, count: int, forced=(), seed: int = 0) -> np.ndarray:
 def first_question_row(w: Workload, k: int) -> int:
     """Row index (after compaction) of the first question token."""
     return min(k, w.n_doc)
+
+
+# ----------------------------------------------------------------------------------------
+# kept-row projection weights (the step after the gather)
+# ----------------------------------------------------------------------------------------
+def qkv_weights(w: Workload) -> np.ndarray:
+    """W_qkv [(Hq + 2 Hkv) d, d_model] ~ N(0, 1/d_model), stored in the workload dtype."""
+    n_feat = (w.n_q_heads + 2 * w.n_kv_heads) * w.head_dim
+    w32 = _normal_rows(rng(w.seed, STREAM_WQKV), n_feat, (w.d_model,))
+    w32 *= np.float32(1.0 / np.sqrt(w.d_model))
+    return _store(w32, w.dtype)

@@ -47,6 +47,9 @@ def lib():
     lib.tg_gated_attention_backward_workspace_bytes.argtypes = [i64, i32, i32, i32]
     lib.tg_gated_attention_backward.argtypes = [i32, i64, i32, i32, i32, p, p, p, p, p, p, f32, p, p, p,
                                                 p, p, p, p, p, p, p, sz, p]
+    lib.tg_qkv_rope_workspace_bytes.restype = sz
+    lib.tg_qkv_rope_workspace_bytes.argtypes = [i64, i32]
+    lib.tg_qkv_rope.argtypes = [i32, i64, i32, p, i64, p, p, i32, i32, i32, p, f32, p, p, p, p, i64, i64, p, sz, p]
     return lib
 
 
@@ -191,3 +194,33 @@ def test_attention_lse_and_backward_validation(lib):
     assert bwd(d=96) == TG_ERR_UNSUPPORTED
     assert bwd(dq=ctypes.c_void_p((1 << 20) + 4)) == TG_ERR_UNSUPPORTED
     assert bwd(m=0) == TG_OK
+
+
+def test_qkv_rope_validation(lib):
+    f = ctypes.c_float
+    need = lib.tg_qkv_rope_workspace_bytes(1000, 128)
+    assert need == 1000 * 64 * 8 + (256 - (1000 * 64 * 8) % 256) % 256
+    assert lib.tg_qkv_rope_workspace_bytes(-1, 128) == 0
+    ws = ctypes.c_void_p(1 << 20)
+
+    def call(**kw):
+        return lib.tg_qkv_rope(
+            kw.get("dt", 1), kw.get("m", 1000), kw.get("dm", 2048), FAKE, kw.get("ldx", 2048), FAKE,
+            kw.get("b", None), kw.get("hq", 16), kw.get("hkv", 8), kw.get("d", 128), kw.get("pos", FAKE),
+            f(kw.get("theta", 1e6)), FAKE, FAKE, FAKE, None, kw.get("slot0", 0), kw.get("cap", 1000),
+            kw.get("ws", ws), kw.get("wsb", need), None)
+
+    assert call(ldx=1000) == TG_ERR_INVALID_ARG
+    assert call(theta=1.0) == TG_ERR_INVALID_ARG
+    assert call(theta=float("nan")) == TG_ERR_INVALID_ARG
+    assert call(slot0=1, cap=1000) == TG_ERR_INVALID_ARG         # slot0 + m > capacity
+    assert call(slot0=-1) == TG_ERR_INVALID_ARG
+    assert call(pos=None) == TG_ERR_INVALID_ARG
+    assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == TG_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == TG_ERR_WORKSPACE
+    assert call(dt=0) == TG_ERR_UNSUPPORTED
+    assert call(d=96) == TG_ERR_UNSUPPORTED
+    assert call(dm=2000, ldx=2000) == TG_ERR_UNSUPPORTED          # d_model not a multiple of 64
+    assert call(d=64, hq=3, hkv=1) == TG_ERR_UNSUPPORTED           # (Hq + 2 Hkv) d not a multiple of 128
+    assert call(b=ctypes.c_void_p((1 << 20) + 4)) == TG_ERR_UNSUPPORTED
+    assert call(m=0, cap=0) == TG_OK

@@ -8,11 +8,11 @@ on the CPU against torch autograd and finite differences.
 Tolerances (bf16 operands, float32 accumulation, bf16 dq/dk/dv):
   dq, dk, dv, ds_kept   max-abs <= 3e-2 max|ref| + 1e-5, mean-abs <= 1e-2 mean|ref| + 1e-6
   dgain[h], dtau        |err| <= 2e-2 of the same sum over absolute terms, + 1e-4
-Three roundings bound each gradient term: the scaled logit operand in bf16 (a
-relative 2^-9 per element, about 0.3% on P at unit-scale logits), P and dZ packed
-to bf16 as MFMA operands (2^-9) and the bf16 result (2^-9): about 0.8% at worst,
-hence 1e-2 on the mean; 3e-2 of the largest value leaves room for the worst
-element.  dgain and dtau are sums whose terms cancel (each row of dZ sums to zero),
+Three roundings bound each gradient term: the forward's scaled query operand in
+bf16 (unit roundoff 2^-8 per element, a few 1e-3 on P at unit-scale logits), P and
+dZ packed to bf16 as MFMA operands (2^-8) and the bf16 result (2^-8): below 1% on
+average, hence 1e-2 on the mean; 3e-2 of the largest value leaves room for the
+worst element.  dgain and dtau are sums whose terms cancel (each row of dZ sums to zero),
 so their error is judged against the sum of the terms' magnitudes, not against the
 (possibly tiny) result; the absolute floors cover float32 rounding of results that
 are exactly zero (a single visible key gives dZ = 0).
