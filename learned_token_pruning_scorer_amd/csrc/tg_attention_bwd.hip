@@ -11,58 +11,67 @@
 //     dQ = dZ K / (sqrt(d) tau),  dK = dZ^T Q / (sqrt(d) tau),  dV = P^T dO
 //     ds[j] = sum_h gain[h] sum_i dZ_h[i,j],  dgain[h] = sum_j s[j] sum_i dZ_h[i,j]
 //     dtau = -(1/tau) sum dZ . (q.k / (sqrt(d) tau))
-// P is recomputed from the forward's row log-sum-exp.
+// P is recomputed from the forward's row log-sum-exp: P = exp2(c2 q.k + g2 s - lse2)
+// with c2 = log2(e) / (sqrt(d) tau), g2 = gain log2(e), lse2 = lse log2(e); the
+// product q.k is exact in float32 from the bf16 operands and the scale is applied in
+// float32.
 //
-// Kernels (bf16 MFMA 32x32x16, float32 accumulation):
-//  * dot: D[i,h] = dO_i . O_i;
+// Kernels (bf16 MFMA 32x32x16, float32 accumulation), the streamed tiles fed by DMA
+// (global_load_lds) into double-buffered, XOR-swizzled LDS: the next tile is in
+// flight while the current one is consumed, one barrier per tile.
+//  * prep: D[h, i] = dO_i . O_i and lse2[h, i], head-major so a tile's values are
+//    contiguous;
 //  * dq:  the forward's shape -- a wave owns 32 queries of one head with Q^T and dO^T
-//         as fixed B operands; 32-key K/V tiles stream through LDS; S^T = K Q'^T and
-//         dP^T = V dO^T give dZ^T in registers (lane = query), and dQ^T += K^T dZ^T
-//         reads K^T from the tile with ds_read_b64_tr_b16 exactly as the forward reads V^T;
-//  * dkv: the transpose -- a wave owns 32 keys of one key/value head; the workgroup's
-//         K' and V rows stay in LDS as the waves' fixed B operands; 32-query Q/dO tiles of
-//         every head of the group stream through LDS; S = Q K'^T and dP = dO V^T give
-//         dZ in registers (lane = key), dV^T += dO^T P and dK^T += Q^T dZ read dO^T and
-//         Q^T from the tiles by transposing LDS reads.  The key-side sums (ds, dgain,
-//         dtau) accumulate per lane and are reduced at the end;
-//  * reduce: sums the per-workgroup partials of ds (over key/value heads), dgain and
-//         dtau in a fixed order, so results are deterministic.
+//         as fixed B operands in registers; 64-key K/V tiles stream through LDS; per
+//         32 keys, S^T = K Q^T and dP^T = V dO^T give dZ^T in registers (lane =
+//         query), and dQ^T += K^T dZ^T reads K^T from the tile with ds_read_b64_tr_b16;
+//  * dkv: the transpose, on 16x16x32 MFMA -- a workgroup (8 waves, two per SIMD) owns
+//         128 keys of one key/value head and a wave 16 of them, with K and V as fixed B
+//         operands in registers and the dK / dV accumulators beside them (about 120
+//         registers, so two waves share a SIMD and hide each other's latencies);
+//         32-query Q / dO tiles of every head of the group stream through a 3-stage LDS
+//         ring; S = Q K^T and dP = dO V^T give P and dZ (lane = key), dV^T += dO^T P and
+//         dK^T += Q^T dZ read dO^T and Q^T from the tiles by transposing LDS reads.  The
+//         key-side sums (ds, dgain, dtau) accumulate per lane and leave as
+//         per-workgroup partials;
+//  * reduce: sums the partials of ds (over key/value heads), dgain and dtau in a fixed
+//         order, so results are deterministic.
 // Every gradient element is written by exactly one workgroup: no float atomics.
 #include "tg_common.h"
 
 namespace tg {
 
-constexpr int kBwdWaves = 4;                     // dq workgroup
-constexpr int kDkvWaves = 8;                     // dkv workgroup
-constexpr int kBwdTile = 32;                     // keys (dq) or queries (dkv) per LDS tile
-constexpr int kDkvKeys = 32 * kDkvWaves;         // keys per dkv workgroup
-constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kDqWaves = 4;                      // dq workgroup
+constexpr int kDqKeys = 64;                      // keys per dq tile
+constexpr int kDkvWaves = 8;                     // dkv workgroup (two waves per SIMD)
+constexpr int kDkvKeys = 16 * kDkvWaves;         // keys per dkv workgroup, 16 per wave
+constexpr int kDkvRows = 32;                     // queries per dkv tile
+constexpr int kDkvStages = 3;                    // dkv tiles in flight or in use
 
 typedef short bs16x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // XOR swizzle of the 16-byte chunks of a tile row (row = key or query in the tile)
 template <int D> __device__ __forceinline__ int bwd_swz(int r);
 template <> __device__ __forceinline__ int bwd_swz<128>(int r) { return r & 15; }
 template <> __device__ __forceinline__ int bwd_swz<64>(int r) { return (r >> 1) & 7; }
 
-// Copies `rows` rows of D bf16 (row stride `ld` elements) into a swizzled LDS tile;
-// rows past `valid` repeat the last valid row (their results are masked).
-// With a scale, each element is multiplied by it (in float32) and rounded back to bf16.
+// DMA of `rows` rows of D bf16 (row stride ld elements, first row `first`, rows past
+// `m` re-read row m - 1) into a swizzled LDS tile at byte address `dst`.  A DMA
+// instruction moves 1 KiB = 1024 / (2 D) rows; instruction I of the tile goes to wave
+// I % waves.  Lane L writes physical chunk L % CPR of row RPI I + L / CPR, which holds
+// logical chunk (L % CPR) ^ swz(row).
 template <int D>
-__device__ __forceinline__ void bwd_load_tile(uint16_t* tile, const uint16_t* __restrict__ src, int64_t ld,
-                                              int first, int valid, int rows, float scale = 1.0f,
-                                              bool scaled = false) {
-  constexpr int CPR = D / 8;   // 16-byte chunks per row
-  for (int p = threadIdx.x; p < rows * CPR; p += blockDim.x) {
-    const int r = p / CPR, c = p % CPR;
-    const int rr = min(first + r, valid - 1);
-    u32x4 v = *reinterpret_cast<const u32x4*>(src + (int64_t)rr * ld + 8 * c);
-    if (scaled) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        v[e] = pack_bf16x2(bf16_to_f32(v[e] & 0xffffu) * scale, bf16_to_f32(v[e] >> 16) * scale);
-    }
-    *reinterpret_cast<u32x4*>(&tile[r * D + 8 * (c ^ bwd_swz<D>(r))]) = v;
+__device__ __forceinline__ void bwd_dma_tile(uint32_t dst, const uint16_t* __restrict__ src, int64_t ld, int first,
+                                             int m, int rows, int wave, int waves, int lane) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
+  const int n_inst = rows / RPI;
+  const char* base = reinterpret_cast<const char*>(src + (int64_t)first * ld);
+  for (int I = wave; I < n_inst; I += waves) {
+    const int r = RPI * I + lane / CPR, p = lane % CPR;
+    const int rr = min(first + r, m - 1) - first;
+    const uint32_t off = (uint32_t)(((int64_t)rr * ld + 8 * (p ^ bwd_swz<D>(r))) * 2);
+    dma_lds16(off, base, dst + I * 1024);
   }
 }
 
@@ -72,18 +81,18 @@ __device__ __forceinline__ bf16x8 bwd_row(const uint16_t* tile, int r, int s, in
   return *reinterpret_cast<const bf16x8*>(&tile[r * D + 8 * ((2 * s + half) ^ bwd_swz<D>(r))]);
 }
 
-// Transposed A operand over the tile's rows for a 16-row k-step s2 and d tile u: lane half
-// h receives rows {4h..4h+3, 8+4h..8+4h+3} (+16 s2), the order in which a 32x32
+// Transposed A operand over the tile's rows r0 + 16 s2 .. + 15 and d tile u: lane half
+// h receives rows {4h..4h+3, 8+4h..8+4h+3} (+ r0 + 16 s2), the order in which a 32x32
 // accumulator's registers leave them, at d = 32u + (lane & 31)
 template <int D>
-__device__ __forceinline__ bf16x8 bwd_tr(const uint16_t* tile, int s2, int u, int lane) {
+__device__ __forceinline__ bf16x8 bwd_tr(const uint16_t* tile, int r0, int s2, int u, int lane) {
   const int half = lane >> 5, gi = lane & 15, gg = lane >> 4;
   const int row_lane = 4 * half + (gi >> 2);
   const int dcol = 32 * u + 16 * (gg & 1) + 4 * (gi & 3);
   u32x2 part[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
-    const int row = 16 * s2 + 8 * r + row_lane;
+    const int row = r0 + 16 * s2 + 8 * r + row_lane;
     const int off = row * D + 8 * ((dcol >> 3) ^ bwd_swz<D>(row)) + (dcol & 7);
     part[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                             (__attribute__((address_space(3))) bs16x4*)(&tile[off])));
@@ -101,50 +110,60 @@ __device__ __forceinline__ bf16x8 pack_acc(const f32x16& a, int s2) {
 }
 
 // ---------------------------------------------------------------------------------
-// D[i, h] = dO[i, h, :] . O[i, h, :]
+// D[h, i] = dO[i, h, :] . O[i, h, :] and lse2[h, i] = lse[i, h] log2(e), head-major
 // ---------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dot_kernel(int rows, const uint16_t* __restrict__ o,
-                                                       const uint16_t* __restrict__ dout, float* __restrict__ dsum) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (r >= rows) return;
+__global__ __launch_bounds__(256) void bwd_prep_kernel(int m, int hq, const uint16_t* __restrict__ o,
+                                                        const uint16_t* __restrict__ dout,
+                                                        const float* __restrict__ lse, float* __restrict__ dsum_t,
+                                                        float* __restrict__ lse2_t) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;   // = row * hq + head
+  if (r >= (int64_t)m * hq) return;
   float acc = 0.f;
 #pragma unroll
   for (int c = 0; c < D / 8; ++c) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + (int64_t)r * D + 8 * c);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + (int64_t)r * D + 8 * c);
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + r * D + 8 * c);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + r * D + 8 * c);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       acc = fmaf(bf16_to_f32(a[e] & 0xffffu), bf16_to_f32(b[e] & 0xffffu), acc);
       acc = fmaf(bf16_to_f32(a[e] >> 16), bf16_to_f32(b[e] >> 16), acc);
     }
   }
-  dsum[r] = acc;
+  const int64_t row = r / hq, head = r % hq;
+  dsum_t[head * m + row] = acc;
+  lse2_t[head * m + row] = lse[r] * kLog2e;
 }
 
 // ---------------------------------------------------------------------------------
 // dQ
 // ---------------------------------------------------------------------------------
+template <int D>
+struct DqLds {
+  static constexpr int TILE = kDqKeys * D * 2;                 // bytes of one K or V tile
+  static constexpr int K0 = 0, V0 = TILE, S0 = 2 * TILE, P0 = S0 + kDqKeys * 4, BUF = P0 + kDqKeys * 4;
+  static constexpr int BYTES = 2 * BUF;
+};
+
 template <int D, int HPW>
-__global__ __launch_bounds__(kBwdWaves * 64, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
     int m, int hq, int hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos, const float* __restrict__ s_kept,
-    const float* __restrict__ gain, const float* __restrict__ lse, const float* __restrict__ dsum,
+    const float* __restrict__ gain, const float* __restrict__ lse, const float* __restrict__ dsum_t,
     const uint16_t* __restrict__ dout, float c2, float c_nat, uint16_t* __restrict__ dq, int n_qtiles) {
-  constexpr int ROWS = 32 * kBwdWaves / HPW;
-  __shared__ __attribute__((aligned(16))) uint16_t k_t[kBwdTile * D];
-  __shared__ __attribute__((aligned(16))) uint16_t v_t[kBwdTile * D];
-  __shared__ __attribute__((aligned(16))) float s_t[kBwdTile];
-  __shared__ __attribute__((aligned(16))) int32_t p_t[kBwdTile];
+  using L = DqLds<D>;
+  constexpr int ROWS = 32 * kDqWaves / HPW;
+  __shared__ __attribute__((aligned(1024))) char lds[L::BYTES];
+  const uint32_t lds0 = lds_addr(lds);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
   const int group = hq / hkv;
   const int slots_per_kv = group / HPW;
   const int units = hkv * slots_per_kv;
   const int unit = blockIdx.x % units;
-  const int qt = n_qtiles - 1 - blockIdx.x / units;
+  const int qt = n_qtiles - 1 - blockIdx.x / units;             // longest first
   const int kvh = unit / slots_per_kv;
   const int head = kvh * group + (unit % slots_per_kv) * HPW + wave % HPW;
   const int q0 = qt * ROWS + (wave / HPW) * 32;
@@ -153,22 +172,20 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void bwd_dq_kernel(
   const int wave_last = min(m - 1, q0 + 31);
   const bool live_row = row < m;
 
-  // fixed B operands: Q' = c2 Q (base-2 logits) and dO, lane = query row
+  // fixed B operands: Q and dO, lane = query row
   bf16x8 qf[D / 16], df[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     if (live_row) {
-      const bf16x8 raw = *reinterpret_cast<const bf16x8*>(q + ((int64_t)row * hq + head) * D + 16 * s + 8 * half);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<__bf16>(static_cast<float>(raw[e]) * c2);
+      qf[s] = *reinterpret_cast<const bf16x8*>(q + ((int64_t)row * hq + head) * D + 16 * s + 8 * half);
       df[s] = *reinterpret_cast<const bf16x8*>(dout + ((int64_t)row * hq + head) * D + 16 * s + 8 * half);
     } else {
       qf[s] = bf16x8{};
       df[s] = bf16x8{};
     }
   }
-  const float lse2 = live_row ? lse[(int64_t)row * hq + head] * kLog2e : 0.f;
-  const float dval = live_row ? dsum[(int64_t)row * hq + head] : 0.f;
+  const float nlse2 = live_row ? -lse[(int64_t)row * hq + head] * kLog2e : 0.f;
+  const float dval = live_row ? dsum_t[(int64_t)head * m + row] : 0.f;
   const int32_t qpos = live_row ? (pos ? pos[row] : row) : INT32_MIN;
   const float g2 = s_kept ? gain[head] * kLog2e : 0.f;
 
@@ -179,47 +196,68 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void bwd_dq_kernel(
     for (int i = 0; i < 16; ++i) dqa[u][i] = 0.f;
 
   const int rows_end = min(m, (qt + 1) * ROWS);
-  const int n_tiles = (rows_end + kBwdTile - 1) / kBwdTile;
+  const int n_tiles = (rows_end + kDqKeys - 1) / kDqKeys;
+  const uint16_t* kh = k + (int64_t)kvh * D;
+  const uint16_t* vh = v + (int64_t)kvh * D;
+  const int64_t ld = (int64_t)hkv * D;
+
+  auto issue = [&](int t) {
+    const int kb = t * kDqKeys;
+    const uint32_t buf = lds0 + (t & 1) * L::BUF;
+    bwd_dma_tile<D>(buf + L::K0, kh, ld, kb, m, kDqKeys, wave, kDqWaves, lane);
+    bwd_dma_tile<D>(buf + L::V0, vh, ld, kb, m, kDqKeys, (wave + 2) % kDqWaves, kDqWaves, lane);
+    const uint32_t off = (uint32_t)((min(kb + lane, m - 1) - kb) * 4);
+    if (wave == 0 && s_kept) dma_lds4(off, s_kept + kb, buf + L::S0);
+    if (wave == 1 && pos) dma_lds4(off, pos + kb, buf + L::P0);
+  };
+
+  if (n_tiles > 0) issue(0);
   for (int t = 0; t < n_tiles; ++t) {
-    const int kb = t * kBwdTile;
-    __syncthreads();   // the previous tile is no longer read
-    bwd_load_tile<D>(k_t, k + (int64_t)kvh * D, (int64_t)hkv * D, kb, m, kBwdTile);
-    bwd_load_tile<D>(v_t, v + (int64_t)kvh * D, (int64_t)hkv * D, kb, m, kBwdTile);
-    if (tid < kBwdTile) {
-      const int key = kb + tid, kc = min(key, m - 1);
-      s_t[tid] = s_kept ? s_kept[kc] : 0.f;
-      p_t[tid] = key < m ? (pos ? pos[kc] : kc) : INT32_MAX;
-    }
-    __syncthreads();
-    if (!(wave_live && kb <= wave_last)) continue;
-    f32x16 sa, da;
+    const int kb = t * kDqKeys;
+    dma_wait_all();
+    __syncthreads();   // tile t visible to every wave; tile t - 1's buffer free
+    if (t + 1 < n_tiles) issue(t + 1);
+    if (!wave_live || kb > wave_last) continue;
+    const char* buf = lds + (t & 1) * L::BUF;
+    const uint16_t* k_t = reinterpret_cast<const uint16_t*>(buf + L::K0);
+    const uint16_t* v_t = reinterpret_cast<const uint16_t*>(buf + L::V0);
+    const float* s_t = reinterpret_cast<const float*>(buf + L::S0);
+    const int32_t* p_t = reinterpret_cast<const int32_t*>(buf + L::P0);
+#pragma unroll 1
+    for (int h2 = 0; h2 < kDqKeys / 32; ++h2) {
+      const int kb2 = kb + 32 * h2;
+      if (kb2 > wave_last) break;
+      f32x16 sa, da;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { sa[i] = 0.f; da[i] = 0.f; }
+      for (int i = 0; i < 16; ++i) { sa[i] = 0.f; da[i] = 0.f; }
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(k_t, l32, s, half), qf[s], sa, 0, 0, 0);
-      da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(v_t, l32, s, half), df[s], da, 0, 0, 0);
-    }
-    // register e holds key j = 8 (e/4) + 4 half + e%4 of the tile, query = this lane's row
-    f32x16 dz;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int j0 = 8 * g + 4 * half;
-      const f32x4 sv = *reinterpret_cast<const f32x4*>(&s_t[j0]);
-      typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-      const i32x4 kp = *reinterpret_cast<const i32x4*>(&p_t[j0]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int e = 4 * g + r;
-        const float p = kp[r] <= qpos ? __builtin_amdgcn_exp2f(sa[e] + g2 * sv[r] - lse2) : 0.f;
-        dz[e] = p * (da[e] - dval);
+      for (int s = 0; s < D / 16; ++s) {
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(k_t, 32 * h2 + l32, s, half), qf[s], sa, 0, 0, 0);
+        da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(v_t, 32 * h2 + l32, s, half), df[s], da, 0, 0, 0);
       }
-    }
-    const bf16x8 z0 = pack_acc(dz, 0), z1 = pack_acc(dz, 1);
+      // register e holds key kb2 + 8 (e/4) + 4 half + e%4, query = this lane's row
 #pragma unroll
-    for (int u = 0; u < D / 32; ++u) {
-      dqa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(k_t, 0, u, lane), z0, dqa[u], 0, 0, 0);
-      dqa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(k_t, 1, u, lane), z1, dqa[u], 0, 0, 0);
+      for (int g = 0; g < 4; ++g) {
+        const int j0 = 32 * h2 + 8 * g + 4 * half;
+        f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+        if (s_kept) sv = *reinterpret_cast<const f32x4*>(&s_t[j0]);
+        i32x4 kp;
+        if (pos) kp = *reinterpret_cast<const i32x4*>(&p_t[j0]);
+        else kp = i32x4{kb + j0, kb + j0 + 1, kb + j0 + 2, kb + j0 + 3};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * g + r;
+          const bool vis = kp[r] <= qpos && kb + j0 + r < m;
+          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sa[e], c2, fmaf(g2, sv[r], nlse2))) : 0.f;
+          da[e] = p * (da[e] - dval);   // da now holds dZ
+        }
+      }
+      const bf16x8 z0 = pack_acc(da, 0), z1 = pack_acc(da, 1);
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u) {
+        dqa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(k_t, 32 * h2, 0, u, lane), z0, dqa[u], 0, 0, 0);
+        dqa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(k_t, 32 * h2, 1, u, lane), z1, dqa[u], 0, 0, 0);
+      }
     }
   }
   if (live_row) {
@@ -237,145 +275,216 @@ __global__ __launch_bounds__(kBwdWaves * 64, 2) void bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------------
-// dK, dV and the key-side partial sums
+// dK, dV and the key-side partial sums (v_mfma_f32_16x16x32_bf16: A 16 rows x 32 k and
+// B 32 k x 16 columns hold row / column lane % 16 and k = 8 (lane / 16) + 0..7; the
+// 16x16 result holds column lane % 16 and rows 4 (lane / 16) + 0..3)
 // ---------------------------------------------------------------------------------
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// A-operand row read for the 16x16x32 shape: row r, k-step s (32 wide), lane group G
+template <int D>
+__device__ __forceinline__ bf16x8 bwd_row16(const uint16_t* tile, int r, int s, int grp) {
+  return *reinterpret_cast<const bf16x8*>(&tile[r * D + 8 * ((4 * s + grp) ^ bwd_swz<D>(r))]);
+}
+
+// Transposed A operand for the 16x16x32 shape over a 32-row tile: lane group G receives
+// rows {4G..4G+3, 16+4G..16+4G+3}, the rows a 16x16 result leaves in its two row blocks,
+// at d = 16 t + (lane & 15)
+template <int D>
+__device__ __forceinline__ bf16x8 bwd_tr16(const uint16_t* tile, int t, int lane) {
+  const int grp = lane >> 4, gi = lane & 15;
+  const int dcol = 16 * t + 4 * (gi & 3);
+  u32x2 part[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int row = 16 * r + 4 * grp + (gi >> 2);
+    const int off = row * D + 8 * ((dcol >> 3) ^ bwd_swz<D>(row)) + (dcol & 7);
+    part[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                            (__attribute__((address_space(3))) bs16x4*)(&tile[off])));
+  }
+  const u32x4 a4 = {part[0][0], part[0][1], part[1][0], part[1][1]};
+  return __builtin_bit_cast(bf16x8, a4);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x4_t& a, const f32x4_t& b) {
+  const u32x4 w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+template <int D>
+struct DkvLds {
+  static constexpr int TILE = kDkvRows * D * 2;                // bytes of one Q or dO tile
+  static constexpr int Q0 = 0, O0 = TILE, ST0 = 2 * TILE;      // stats: lse2[32] | D[32] | pos[32]
+  static constexpr int BUF = ST0 + 3 * kDkvRows * 4 + 128;     // (+ the unused upper half of the pos DMA)
+  static constexpr int BYTES = kDkvStages * BUF;
+};
+
 template <int D>
 __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
     int m, int hq, int hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos, const float* __restrict__ s_kept,
-    const float* __restrict__ gain, const float* __restrict__ lse, const float* __restrict__ dsum,
-    const uint16_t* __restrict__ dout, float c2, float c_nat, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    float* __restrict__ ds_part, float* __restrict__ dgain_part, float* __restrict__ dtau_part, int n_kblocks) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_b[kDkvKeys * D];     // this workgroup's K' = c2 K rows
-  __shared__ __attribute__((aligned(16))) uint16_t v_b[kDkvKeys * D];     // and V rows
-  __shared__ __attribute__((aligned(16))) uint16_t q_t[kBwdTile * D];
-  __shared__ __attribute__((aligned(16))) uint16_t o_t[kBwdTile * D];     // dO tile
-  __shared__ __attribute__((aligned(16))) float lse_t[kBwdTile];
-  __shared__ __attribute__((aligned(16))) float d_t[kBwdTile];
-  __shared__ __attribute__((aligned(16))) int32_t p_t[kBwdTile];
+    const float* __restrict__ gain, const float* __restrict__ stats, int64_t dsum_off, const uint16_t* __restrict__ dout,
+    float c2, float c_nat, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, float* __restrict__ ds_part,
+    float* __restrict__ dgain_part, float* __restrict__ dtau_part, int n_kblocks) {
+  using L = DkvLds<D>;
+  constexpr int KS = D / 32;                      // 32-wide k-steps over d
+  constexpr int DT = D / 16;                      // 16-wide d tiles of dK / dV
+  __shared__ __attribute__((aligned(1024))) char lds[L::BYTES];
+  const uint32_t lds0 = lds_addr(lds);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, l32 = lane & 31;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4, l16 = lane & 15;
   const int group = hq / hkv;
   const int kvh = blockIdx.x % hkv;
   const int kblk = blockIdx.x / hkv;              // longest (earliest keys) first
   const int kb0 = kblk * kDkvKeys;
-  const int kw0 = kb0 + 32 * wave;                // this wave's first key
-  const int key = kw0 + l32;
+  const int kw0 = kb0 + 16 * wave;                // this wave's first key
+  const int key = kw0 + l16;
   const bool live_key = key < m;
   const int kc = min(key, m - 1);
   const int32_t kpos = live_key ? (pos ? pos[kc] : kc) : INT32_MAX;
   const float sk = s_kept ? s_kept[kc] : 0.f;
 
-  // the workgroup's keys: K' = c2 K and V, read by each wave as its fixed B operands
-  bwd_load_tile<D>(k_b, k + (int64_t)kvh * D, (int64_t)hkv * D, kb0, m, kDkvKeys, c2, true);
-  bwd_load_tile<D>(v_b, v + (int64_t)kvh * D, (int64_t)hkv * D, kb0, m, kDkvKeys);
+  // fixed B operands: K and V of this lane's key, d = 32 s + 8 G + 0..7
+  bf16x8 kf[KS], vf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    kf[s] = *reinterpret_cast<const bf16x8*>(k + ((int64_t)kc * hkv + kvh) * D + 32 * s + 8 * grp);
+    vf[s] = *reinterpret_cast<const bf16x8*>(v + ((int64_t)kc * hkv + kvh) * D + 32 * s + 8 * grp);
+  }
 
-  f32x16 dka[D / 32], dva[D / 32];
+  f32x4_t dka[DT], dva[DT];
 #pragma unroll
-  for (int u = 0; u < D / 32; ++u)
+  for (int t = 0; t < DT; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { dka[u][i] = 0.f; dva[u][i] = 0.f; }
+    for (int i = 0; i < 4; ++i) { dka[t][i] = 0.f; dva[t][i] = 0.f; }
   float ds_acc = 0.f, dtau_acc = 0.f;
 
-  const int first_tile = kb0 / kBwdTile;          // queries before the first key see none of them
-  const int n_tiles = (m + kBwdTile - 1) / kBwdTile;
-  for (int hh = 0; hh < group; ++hh) {
-    const int head = kvh * group + hh;
-    const float g2 = s_kept ? gain[head] * kLog2e : 0.f;
-    const float bias2 = g2 * sk;
-    float col = 0.f;   // sum over queries of dZ for this lane's key and this head
-    for (int t = first_tile; t < n_tiles; ++t) {
-      const int qb = t * kBwdTile;
-      __syncthreads();   // the previous tile is no longer read
-      bwd_load_tile<D>(q_t, q + (int64_t)head * D, (int64_t)hq * D, qb, m, kBwdTile);
-      bwd_load_tile<D>(o_t, dout + (int64_t)head * D, (int64_t)hq * D, qb, m, kBwdTile);
-      if (tid < kBwdTile) {
-        const int qi = qb + tid, qc = min(qi, m - 1);
-        lse_t[tid] = lse[(int64_t)qc * hq + head] * kLog2e;
-        d_t[tid] = dsum[(int64_t)qc * hq + head];
-        p_t[tid] = qi < m ? (pos ? pos[qc] : qc) : INT32_MIN;
-      }
-      __syncthreads();
-      if (qb + kBwdTile - 1 < kw0 || kw0 >= m) continue;   // no query of the tile sees these keys
-      f32x16 sa, da;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { sa[i] = 0.f; da[i] = 0.f; }
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(q_t, l32, s, half),
-                                                     bwd_row<D>(k_b, 32 * wave + l32, s, half), sa, 0, 0, 0);
-        da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(o_t, l32, s, half),
-                                                     bwd_row<D>(v_b, 32 * wave + l32, s, half), da, 0, 0, 0);
-        if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // bounds the operand reads in flight
-      }
-      // register e holds query i = 8 (e/4) + 4 half + e%4 of the tile, key = this lane's.
-      // P is finished and fed to dV before dZ is formed, so the two never share registers.
-      typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-      f32x16 p;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int i0 = 8 * g + 4 * half;
-        const f32x4 lv = *reinterpret_cast<const f32x4*>(&lse_t[i0]);
-        const i32x4 qp = *reinterpret_cast<const i32x4*>(&p_t[i0]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * g + r;
-          p[e] = kpos <= qp[r] ? __builtin_amdgcn_exp2f(sa[e] + bias2 - lv[r]) : 0.f;
-        }
-      }
-      {
-        const bf16x8 p0 = pack_acc(p, 0), p1 = pack_acc(p, 1);
-#pragma unroll
-        for (int u = 0; u < D / 32; ++u) {
-          dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(o_t, 0, u, lane), p0, dva[u], 0, 0, 0);
-          dva[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(o_t, 1, u, lane), p1, dva[u], 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 dv4 = *reinterpret_cast<const f32x4*>(&d_t[8 * g + 4 * half]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * g + r;
-          const float z = p[e] * (da[e] - dv4[r]);
-          col += z;
-          dtau_acc = fmaf(z, sa[e], dtau_acc);
-          da[e] = z;   // da now holds dZ
-        }
-      }
-      const bf16x8 z0 = pack_acc(da, 0), z1 = pack_acc(da, 1);
-#pragma unroll
-      for (int u = 0; u < D / 32; ++u) {
-        dka[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(q_t, 0, u, lane), z0, dka[u], 0, 0, 0);
-        dka[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(q_t, 1, u, lane), z1, dka[u], 0, 0, 0);
-      }
+  const int first_tile = kb0 / kDkvRows;          // queries before the first key see none of them
+  const int n_qt = (m + kDkvRows - 1) / kDkvRows;
+  const int per_head = n_qt - first_tile;
+  const int n_it = group * per_head;
+  const int64_t ld = (int64_t)hq * D;
+  // DMAs this wave issues per tile (its share of the Q and dO rows, plus the statistics)
+  constexpr int PER16 = 2 * (kDkvRows * D * 2 / 1024) / kDkvWaves;
+  static_assert(PER16 >= 1 && (2 * (kDkvRows * D * 2 / 1024)) % kDkvWaves == 0, "tile DMAs split evenly");
+  const bool extra = wave == 0 || (wave == 1 && pos);
+
+  auto issue = [&](int it) {
+    const int hh = it / per_head, t = first_tile + it % per_head;
+    const int head = kvh * group + hh, qb = t * kDkvRows;
+    const uint32_t buf = lds0 + (it % kDkvStages) * L::BUF;
+    bwd_dma_tile<D>(buf + L::Q0, q + (int64_t)head * D, ld, qb, m, kDkvRows, wave, kDkvWaves, lane);
+    bwd_dma_tile<D>(buf + L::O0, dout + (int64_t)head * D, ld, qb, m, kDkvRows, (wave + kDkvWaves / 2) % kDkvWaves,
+                    kDkvWaves, lane);
+    const int qi = min(qb + (lane & 31), m - 1);
+    if (wave == 0) {   // lanes 0..31: lse2[head][qi], lanes 32..63: D[head][qi]
+      const uint32_t off = (uint32_t)(((int64_t)head * m + qi) * 4 + (lane >= 32 ? dsum_off : 0));
+      dma_lds4(off, stats, buf + L::ST0);
     }
-    // this head's key-side sums: both lane halves hold parts of the same key's column
-    col += swap_halves(col);
-    ds_acc = fmaf(s_kept ? gain[head] : 0.f, col, ds_acc);
-    float gsum = (half == 0 && live_key) ? sk * col : 0.f;
+    if (wave == 1 && pos) dma_lds4((uint32_t)(qi * 4), pos, buf + L::ST0 + 2 * kDkvRows * 4);
+  };
+
+  for (int i = 0; i < kDkvStages - 1; ++i)
+    if (i < n_it) issue(i);
+  float col = 0.f;   // this lane's part of the sum over queries of dZ, current head
+  for (int it = 0; it < n_it; ++it) {
+    const int hh = it / per_head, t = first_tile + it % per_head;
+    const int head = kvh * group + hh, qb = t * kDkvRows;
+    // tile it has landed once the DMAs of the later tiles already issued are all that remain
+    const int later = min(kDkvStages - 2, n_it - 1 - it);
+    if (later == 1) {
+      if (extra) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER16 + 1) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" :: "n"(PER16) : "memory");
+    } else {
+      dma_wait_all();
+    }
+    __syncthreads();   // tile it visible to every wave; the buffer of tile it - 1 is free
+    if (it + kDkvStages - 1 < n_it) issue(it + kDkvStages - 1);
+    if (qb + kDkvRows - 1 >= kw0 && kw0 < m) {   // some query of the tile sees these keys
+      const char* buf = lds + (it % kDkvStages) * L::BUF;
+      const uint16_t* q_t = reinterpret_cast<const uint16_t*>(buf + L::Q0);
+      const uint16_t* o_t = reinterpret_cast<const uint16_t*>(buf + L::O0);
+      const float* lse_t = reinterpret_cast<const float*>(buf + L::ST0);
+      const float* d_t = lse_t + kDkvRows;
+      const int32_t* p_t = reinterpret_cast<const int32_t*>(d_t + kDkvRows);
+      const float bias2 = s_kept ? gain[head] * kLog2e * sk : 0.f;
+      // S = Q K^T and dP = dO V^T for the tile's two 16-query blocks
+      f32x4_t sa[2], da[2];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) gsum += __shfl_xor(gsum, o, 64);
-    if (lane == 0) dgain_part[((int64_t)head * n_kblocks + kblk) * kDkvWaves + wave] = gsum;
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { sa[b][i] = 0.f; da[b][i] = 0.f; }
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          sa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwd_row16<D>(q_t, 16 * b + l16, s, grp), kf[s], sa[b], 0, 0,
+                                                          0);
+          da[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwd_row16<D>(o_t, 16 * b + l16, s, grp), vf[s], da[b], 0, 0,
+                                                          0);
+        }
+      // register i of block b holds query qb + 16 b + 4 G + i, key = this lane's
+      f32x4_t p[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int i0 = 16 * b + 4 * grp;
+        const f32x4_t lv = *reinterpret_cast<const f32x4_t*>(&lse_t[i0]);
+        i32x4 qp;
+        if (pos) qp = *reinterpret_cast<const i32x4*>(&p_t[i0]);
+        else qp = i32x4{qb + i0, qb + i0 + 1, qb + i0 + 2, qb + i0 + 3};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool vis = kpos <= qp[i] && qb + i0 + i < m;
+          p[b][i] = vis ? __builtin_amdgcn_exp2f(fmaf(sa[b][i], c2, bias2 - lv[i])) : 0.f;
+        }
+      }
+      const bf16x8 pb = pack8(p[0], p[1]);
+#pragma unroll
+      for (int t2 = 0; t2 < DT; ++t2)
+        dva[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwd_tr16<D>(o_t, t2, lane), pb, dva[t2], 0, 0, 0);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(&d_t[16 * b + 4 * grp]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float z = p[b][i] * (da[b][i] - dv4[i]);
+          col += z;
+          dtau_acc = fmaf(z, sa[b][i], dtau_acc);
+          da[b][i] = z;   // da now holds dZ
+        }
+      }
+      const bf16x8 zb = pack8(da[0], da[1]);
+#pragma unroll
+      for (int t2 = 0; t2 < DT; ++t2)
+        dka[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwd_tr16<D>(q_t, t2, lane), zb, dka[t2], 0, 0, 0);
+    }
+    if (t == n_qt - 1) {
+      // this head's key-side sums: the four lane groups hold parts of the same key's column
+      col += __shfl_xor(col, 16, 64);
+      col += __shfl_xor(col, 32, 64);
+      ds_acc = fmaf(s_kept ? gain[head] : 0.f, col, ds_acc);
+      float gsum = (grp == 0 && live_key) ? sk * col : 0.f;
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) gsum += __shfl_xor(gsum, o, 64);
+      if (lane == 0) dgain_part[((int64_t)head * n_kblocks + kblk) * kDkvWaves + wave] = gsum;
+      col = 0.f;
+    }
   }
   if (live_key) {
-    if (half == 0) ds_part[(int64_t)kvh * m + key] = ds_acc;
+    if (grp == 0) ds_part[(int64_t)kvh * m + key] = ds_acc;
     uint16_t* krow = dk + ((int64_t)key * hkv + kvh) * D;
     uint16_t* vrow = dv + ((int64_t)key * hkv + kvh) * D;
 #pragma unroll
-    for (int u = 0; u < D / 32; ++u)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * u + 8 * g + 4 * half;
-        const u32x2 kk = {pack_bf16x2(dka[u][4 * g] * c_nat, dka[u][4 * g + 1] * c_nat),
-                          pack_bf16x2(dka[u][4 * g + 2] * c_nat, dka[u][4 * g + 3] * c_nat)};
-        const u32x2 vv = {pack_bf16x2(dva[u][4 * g], dva[u][4 * g + 1]),
-                          pack_bf16x2(dva[u][4 * g + 2], dva[u][4 * g + 3])};
-        *reinterpret_cast<u32x2*>(krow + d0) = kk;
-        *reinterpret_cast<u32x2*>(vrow + d0) = vv;
-      }
+    for (int t2 = 0; t2 < DT; ++t2) {
+      const int d0 = 16 * t2 + 4 * grp;
+      const u32x2 kk = {pack_bf16x2(dka[t2][0] * c_nat, dka[t2][1] * c_nat),
+                        pack_bf16x2(dka[t2][2] * c_nat, dka[t2][3] * c_nat)};
+      const u32x2 vv = {pack_bf16x2(dva[t2][0], dva[t2][1]), pack_bf16x2(dva[t2][2], dva[t2][3])};
+      *reinterpret_cast<u32x2*>(krow + d0) = kk;
+      *reinterpret_cast<u32x2*>(vrow + d0) = vv;
+    }
   }
   float tsum = live_key ? dtau_acc : 0.f;
 #pragma unroll
@@ -384,11 +493,11 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
 }
 
 // ---------------------------------------------------------------------------------
-// fixed-order sums of the partials
+// Fixed-order sums of the partials.  Blocks 0 .. ceil(m/256)-1 sum ds over the
+// key/value heads; the last block sums dgain (one wave per head) and dtau (the whole
+// block).  Each sum's order is fixed by the launch shape alone, so results are
+// bitwise reproducible.
 // ---------------------------------------------------------------------------------
-// Blocks 0 .. ceil(m/256)-1 sum ds over the key/value heads; the last block sums dgain
-// (one wave per head) and dtau (the whole block).  Each sum's order is fixed by the
-// launch shape alone, so results are bitwise reproducible.
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(int m, int hq, int hkv, int n_kblocks, int n_dkv_blocks,
                                                           const float* __restrict__ ds_part,
                                                           const float* __restrict__ dgain_part,
@@ -430,12 +539,13 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(int m, int hq, int hkv,
 }
 
 struct BwdLayout {
-  size_t dsum, ds_part, dgain_part, dtau_part, bytes;
+  size_t lse2, dsum, ds_part, dgain_part, dtau_part, bytes;
   BwdLayout(int64_t m, int64_t hq, int64_t hkv) {
     const int64_t nkb = (m + kDkvKeys - 1) / kDkvKeys;
     auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
-    dsum = 0;
-    ds_part = up(dsum + (size_t)m * hq * 4);
+    lse2 = 0;                                    // [hq][m]
+    dsum = up(lse2 + (size_t)m * hq * 4);        // [hq][m]
+    ds_part = up(dsum + (size_t)m * hq * 4);     // [hkv][m]
     dgain_part = up(ds_part + (size_t)hkv * m * 4);
     dtau_part = up(dgain_part + (size_t)hq * nkb * kDkvWaves * 4);
     bytes = up(dtau_part + (size_t)hkv * nkb * kDkvWaves * 4);
@@ -444,14 +554,14 @@ struct BwdLayout {
 
 template <int D, int HPW>
 static void launch_bwd_dq(int m, int hq, int hkv, const void* q, const void* k, const void* v, const int32_t* pos,
-                          const float* s_kept, const float* gain, const float* lse, const float* dsum,
+                          const float* s_kept, const float* gain, const float* lse, const float* dsum_t,
                           const void* dout, float c2, float c_nat, void* dq, hipStream_t st) {
-  constexpr int ROWS = 32 * kBwdWaves / HPW;
+  constexpr int ROWS = 32 * kDqWaves / HPW;
   const int n_qtiles = (m + ROWS - 1) / ROWS;
   const int grid = n_qtiles * (hq / HPW);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, HPW>), dim3(grid), dim3(kBwdWaves * 64), 0, st, m, hq, hkv,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, HPW>), dim3(grid), dim3(kDqWaves * 64), 0, st, m, hq, hkv,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), pos, s_kept, gain, lse, dsum,
+                     static_cast<const uint16_t*>(v), pos, s_kept, gain, lse, dsum_t,
                      static_cast<const uint16_t*>(dout), c2, c_nat, static_cast<uint16_t*>(dq), n_qtiles);
 }
 
@@ -461,7 +571,8 @@ static tg_status attention_backward(int m, int hq, int hkv, const void* q, const
                                     const void* out, const float* lse, const void* dout, void* dq, void* dk,
                                     void* dv, float* ds, float* dgain, float* dtau, char* ws, hipStream_t st) {
   const BwdLayout L(m, hq, hkv);
-  float* dsum = reinterpret_cast<float*>(ws + L.dsum);
+  float* lse2_t = reinterpret_cast<float*>(ws + L.lse2);
+  float* dsum_t = reinterpret_cast<float*>(ws + L.dsum);
   float* ds_part = reinterpret_cast<float*>(ws + L.ds_part);
   float* dgain_part = reinterpret_cast<float*>(ws + L.dgain_part);
   float* dtau_part = reinterpret_cast<float*>(ws + L.dtau_part);
@@ -469,25 +580,26 @@ static tg_status attention_backward(int m, int hq, int hkv, const void* q, const
   const float c2 = static_cast<float>(1.4426950408889634 / sd);   // base-2 logit per unit q.k
   const float c_nat = static_cast<float>(1.0 / sd);
 
-  const int rows = m * hq;
-  hipLaunchKernelGGL((bwd_dot_kernel<D>), dim3((rows + 255) / 256), dim3(256), 0, st, rows,
-                     static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), dsum);
+  const int64_t rows = (int64_t)m * hq;
+  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, m, hq,
+                     static_cast<const uint16_t*>(out), static_cast<const uint16_t*>(dout), lse, dsum_t, lse2_t);
   const int group = hq / hkv;
   if (group % 4 == 0)
-    launch_bwd_dq<D, 4>(m, hq, hkv, q, k, v, pos, s_kept, gain, lse, dsum, dout, c2, c_nat, dq, st);
+    launch_bwd_dq<D, 4>(m, hq, hkv, q, k, v, pos, s_kept, gain, lse, dsum_t, dout, c2, c_nat, dq, st);
   else if (group % 2 == 0)
-    launch_bwd_dq<D, 2>(m, hq, hkv, q, k, v, pos, s_kept, gain, lse, dsum, dout, c2, c_nat, dq, st);
+    launch_bwd_dq<D, 2>(m, hq, hkv, q, k, v, pos, s_kept, gain, lse, dsum_t, dout, c2, c_nat, dq, st);
   else
-    launch_bwd_dq<D, 1>(m, hq, hkv, q, k, v, pos, s_kept, gain, lse, dsum, dout, c2, c_nat, dq, st);
+    launch_bwd_dq<D, 1>(m, hq, hkv, q, k, v, pos, s_kept, gain, lse, dsum_t, dout, c2, c_nat, dq, st);
   const int n_kblocks = (m + kDkvKeys - 1) / kDkvKeys;
   const int n_dkv = n_kblocks * hkv;
   hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3(n_dkv), dim3(kDkvWaves * 64), 0, st, m, hq, hkv,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), pos, s_kept, gain, lse, dsum,
-                     static_cast<const uint16_t*>(dout), c2, c_nat, static_cast<uint16_t*>(dk),
-                     static_cast<uint16_t*>(dv), ds_part, dgain_part, dtau_part, n_kblocks);
-  // dtau = -(1/tau) sum dZ . (q.k / (sqrt(d) tau)); the kernel summed dZ . (c2 q.k)
-  const float dtau_scale = static_cast<float>(-kLn2 / (double)tau);
+                     static_cast<const uint16_t*>(v), pos, s_kept, gain, lse2_t,
+                     (int64_t)(L.dsum - L.lse2), static_cast<const uint16_t*>(dout), c2, c_nat,
+                     static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), ds_part, dgain_part, dtau_part,
+                     n_kblocks);
+  // dtau = -(1/tau) sum dZ (q.k / (sqrt(d) tau)); the kernel summed dZ q.k
+  const float dtau_scale = static_cast<float>(-1.0 / (sd * (double)tau));
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((m + 255) / 256 + 1), dim3(256), 0, st, m, hq, hkv, n_kblocks, n_dkv,
                      ds_part, dgain_part, dtau_part, dtau_scale, ds, dgain, dtau);
   TG_CHECK_LAUNCH();
@@ -517,7 +629,8 @@ extern "C" tg_status tg_gated_attention_backward(int32_t dtype, int64_t m, int32
   if ((s_kept == nullptr) != (ds_kept == nullptr) || (gain == nullptr) != (dgain == nullptr)) return TG_ERR_INVALID_ARG;
   if (!std::isfinite(tau) || !(tau > 0.f)) return TG_ERR_INVALID_ARG;
   if (dtype != TG_BF16 || (head_dim != 64 && head_dim != 128)) return TG_ERR_UNSUPPORTED;
-  if (m * n_q_heads > INT32_MAX) return TG_ERR_UNSUPPORTED;   // row indices are 32-bit
+  // the dK/dV kernel's DMA reaches the [Hq][m] float statistics through 32-bit byte offsets
+  if (m * n_q_heads >= (int64_t(1) << 29)) return TG_ERR_UNSUPPORTED;
   if (m == 0) return TG_OK;
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return TG_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return TG_ERR_INVALID_ARG;

@@ -90,6 +90,16 @@ __device__ __forceinline__ void dma_lds16(uint32_t off, const void* base, uint32
                : "=&s"(save) : "s"(m0v), "v"(off), "s"(base) : "memory");
 }
 
+// The same for 4 bytes per lane (global_load_lds_dword): LDS byte m0v + 4 L.
+__device__ __forceinline__ void dma_lds4(uint32_t off, const void* base, uint32_t m0v) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %2, %3\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "s"(m0v), "v"(off), "s"(base) : "memory");
+}
+
+// Wait until every DMA (and any other vector memory access) this wave issued has landed.
+__device__ __forceinline__ void dma_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 }  // namespace tg
 
 #define TG_CHECK_LAUNCH()                                   \

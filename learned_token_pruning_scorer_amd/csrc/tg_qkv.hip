@@ -95,7 +95,9 @@ __global__ __launch_bounds__(kQkvWaves * 64, 1) void qkv_rope_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5, l32 = lane & 31;
-  const int wh = wave / WT, wt = wave % WT;
+  // wave -> (feature half, token slice): the waves of one token slice sit on different
+  // SIMDs, so a ragged last token tile (only its first slices hold tokens) costs less
+  const int wh = wave % T::WH, wt = wave / T::WH;
 
   // workgroup -> (feature tile, token tile): with n_ft a multiple of 8, consecutive
   // workgroups (which the dispatcher sends to the 8 XCDs in turn) take different
@@ -110,6 +112,9 @@ __global__ __launch_bounds__(kQkvWaves * 64, 1) void qkv_rope_kernel(
     tt = blockIdx.x / n_ft;
   }
   const int f0 = ft * kQkvFeat, tok0 = tt * BT;
+  // waves whose tokens or features all lie past the end skip the products (they still
+  // share the loads and barriers)
+  const bool busy = tok0 + 32 * BTW * wt < m && f0 + 128 * wh < n_feat;
 
   // DMA j of this wave fills rows 8 (I wave + j) + lane/8 of the W (or X) stage; the lane
   // writes physical chunk lane%8 of its row, which holds logical chunk (lane%8) ^ swz(row).
@@ -165,6 +170,7 @@ __global__ __launch_bounds__(kQkvWaves * 64, 1) void qkv_rope_kernel(
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();   // chunk c visible to all waves; chunk c - 1's slot free for reuse
     if (c + NS - 1 < nch) issue(c + NS - 1, (slot + NS - 1) % NS);
+    if (!busy) return;
     const char* st = ring + slot * T::STAGE;
 #pragma unroll
     for (int ks = 0; ks < kQkvKC / 16; ++ks) {
