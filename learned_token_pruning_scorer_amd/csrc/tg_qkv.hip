@@ -23,7 +23,7 @@
 //    rotation is element-wise in registers.  Both operands stream through an NS-stage
 //    LDS ring by DMA (64-wide k-chunks, 128-byte rows XOR-swizzled by (row >> 1) & 7 so
 //    the operand reads are conflict-free); the epilogue adds the bias, rotates q and k
-//    with the table and stores bf16 rows.  Feature tiles are spread so that each XCD
+//    with the table and writes bf16 rows through LDS, so each row leaves as whole lines.  Feature tiles are spread so that each XCD
 //    keeps the same two W tiles in its L2 while the token tiles stream past.
 #include <type_traits>
 
@@ -89,7 +89,10 @@ __global__ __launch_bounds__(kQkvWaves * 64, 1) void qkv_rope_kernel(
   constexpr int BT = T::BT, AT = T::AT, WT = T::WT;
   constexpr int HT = D / 64;                 // 32-wide accumulator tiles per half head
   constexpr int HPW = 128 / D;               // heads per wave
-  __shared__ __attribute__((aligned(16))) char ring[NS * T::STAGE];
+  // the ring, reused after the main loop as each wave's output staging area
+  constexpr int SROWS = 32 * BTW, SPITCH = 128 * 2 + 16;   // 16 bytes of padding per row
+  constexpr int RING = NS * T::STAGE, STAGING = kQkvWaves * SROWS * SPITCH;
+  __shared__ __attribute__((aligned(16))) char ring[RING > STAGING ? RING : STAGING];
   const uint32_t lds0 = lds_addr(ring);
 
   const int tid = threadIdx.x;
@@ -196,33 +199,36 @@ __global__ __launch_bounds__(kQkvWaves * 64, 1) void qkv_rope_kernel(
   }
 
   // epilogue: tile (a, b) holds token tok0 + 32 (wt BTW + b) + l32 and features
-  // fw + 32 a + 8 g + 4 half + r (register 4 g + r), fw = the wave's first feature
+  // fw + 32 a + 8 g + 4 half + r (register 4 g + r), fw = the wave's first feature.
+  // Results go through LDS so that each output row leaves as whole 16-byte-per-lane
+  // lines (8-byte scattered stores left partly written lines for L2 to evict).
   const int fw = f0 + 128 * wh;
+  __syncthreads();   // every wave is done with the ring
   if (fw >= n_feat) return;
+  char* stage = ring + wave * SROWS * SPITCH;
+  uint16_t* dst[HPW];
+  int64_t stride[HPW];                                // elements between consecutive tokens
 #pragma unroll
   for (int hp = 0; hp < HPW; ++hp) {
     const int hg = (fw + hp * D) / D;                 // head over the q | k | v concatenation
-    uint16_t* base;
-    int64_t stride;                                   // elements between consecutive tokens
-    bool rotate = true;
+    const bool rotate = hg < hq + hkv;
     if (hg < hq) {
-      base = q_out + (int64_t)hg * D;
-      stride = (int64_t)hq * D;
+      dst[hp] = q_out + (int64_t)hg * D;
+      stride[hp] = (int64_t)hq * D;
     } else if (hg < hq + hkv) {
-      base = k_cache + (slot0 * hkv + (hg - hq)) * D;
-      stride = (int64_t)hkv * D;
+      dst[hp] = k_cache + (slot0 * hkv + (hg - hq)) * D;
+      stride[hp] = (int64_t)hkv * D;
     } else {
-      base = v_cache + (slot0 * hkv + (hg - hq - hkv)) * D;
-      stride = (int64_t)hkv * D;
-      rotate = false;
+      dst[hp] = v_cache + (slot0 * hkv + (hg - hq - hkv)) * D;
+      stride[hp] = (int64_t)hkv * D;
     }
     const float* hb = bias ? bias + (int64_t)hg * D : nullptr;
 #pragma unroll
     for (int b = 0; b < BTW; ++b) {
       const int tok = tok0 + 32 * (wt * BTW + b) + l32;
       const int tc = min(tok, m - 1);
-      uint16_t* row = base + (int64_t)tc * stride;
       const float2* trow = tab + (int64_t)tc * (D / 2);
+      char* srow = stage + (32 * b + l32) * SPITCH + hp * D * 2;
 #pragma unroll
       for (int at = 0; at < HT; ++at) {
         const int alo = hp * 2 * HT + at, ahi = alo + HT;
@@ -248,18 +254,32 @@ __global__ __launch_bounds__(kQkvWaves * 64, 1) void qkv_rope_kernel(
             const f32x4 cs01 = *reinterpret_cast<const f32x4*>(trow + i0);
             const f32x4 cs23 = *reinterpret_cast<const f32x4*>(trow + i0 + 2);
             const float c[4] = {cs01[0], cs01[2], cs23[0], cs23[2]};
-            const float s[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
+            const float sn[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const float a = lo[r], e = hi[r];
-              lo[r] = fmaf(a, c[r], -e * s[r]);
-              hi[r] = fmaf(e, c[r], a * s[r]);
+              lo[r] = fmaf(a, c[r], -e * sn[r]);
+              hi[r] = fmaf(e, c[r], a * sn[r]);
             }
           }
-          if (tok < m) store4(row, i0, D / 2, lo, hi);
+          store4(reinterpret_cast<uint16_t*>(srow), i0, D / 2, lo, hi);
         }
       }
     }
+  }
+  // copy-out: 16 lanes per token row of the wave's 128 features, 4 rows per instruction
+  const int c16 = lane & 15, f = 8 * c16, hp = f / D, fi = f % D;
+  uint16_t* drow = dst[0];
+  int64_t dstride = stride[0];
+#pragma unroll
+  for (int h = 1; h < HPW; ++h)
+    if (hp == h) { drow = dst[h]; dstride = stride[h]; }
+#pragma unroll
+  for (int j = 0; j < SROWS / 4; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    const int tok = tok0 + 32 * wt * BTW + r;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * SPITCH + 16 * c16);
+    if (tok < m) *reinterpret_cast<u32x4*>(drow + (int64_t)tok * dstride + fi) = val;
   }
 }
 
