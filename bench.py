@@ -31,9 +31,9 @@ CALIB_BYTES = 1 << 30          # streaming copy in --profile-steps mode: reads a
 # HBM bytes per launch of the attention kernel on long128k, from rocprofv3 FETCH_SIZE and WRITE_SIZE
 # scaled by the same counters' reading of the calibration copy (profiles/long128k_hbm_counters.md).
 # Reported only while the kernel source is the one the counters were taken on.
-ATTN_TRAFFIC = {"workload": "long128k", "bytes": 114899275,
+ATTN_TRAFFIC = {"workload": "long128k", "bytes": 118034734,
                 "source": "learned_token_pruning_scorer_amd/csrc/tg_attention.hip",
-                "sha256": "8ea07288da4ac9ff416aa39ab0e62a5b6bcc6fa75ce39c591b41951dc1b69139"}
+                "sha256": "455ecfd498a2c83f47205d6dab4b4dce7de2771e1bffce65f47e103035a52de4"}
 
 
 def parse():
@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--also", default="niah16k", help="second workload reported beside the main one ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-score-rows", type=int, default=131072)
-    ap.add_argument("--cpu-attn-rows", type=int, default=8192)
+    ap.add_argument("--cpu-attn-rows", type=int, default=0, help="query rows of the CPU attention sample (0 = all)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the timings of the attention backward and the multi-budget / random selectors")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -238,7 +238,7 @@ def cpu_baseline(name, score_rows, attn_rows):
     t_gather = time.perf_counter() - t
     ai = inputs.attention_inputs(w, kept)
     m = len(kept)
-    arows = inputs.sample_rows(m, min(attn_rows, m), forced=(0, m - 1), seed=1)
+    arows = inputs.sample_rows(m, m if attn_rows <= 0 else min(attn_rows, m), forced=(0, m - 1), seed=1)
     q64, k64, v64 = (inputs.to_f64(a, w.dtype) for a in (ai.q, ai.k, ai.v))
     t = time.perf_counter()
     oracle.gated_attention(q64, k64, v64, kept, s_full[kept], ai.gain, ai.tau, rows=arows)
@@ -251,8 +251,10 @@ def cpu_baseline(name, score_rows, attn_rows):
     measured = t_score * (len(rows) / w.n) + t_select + t_gather + t_attn_sample
     return {"value": w.n / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"{name}: gate score on {len(rows)} of {w.n} rows, full select and gather, "
-                       f"attention on {len(arows)} of {m} query rows; each scaled to the full workload "
-                       f"(score by rows, attention by causal key count); {measured:.1f} s of CPU time measured"),
+                       f"attention on {len(arows)} of {m} query rows"
+                       + ("" if len(rows) == w.n and len(arows) == m else
+                          "; each scaled to the full workload (score by rows, attention by causal key count)")
+                       + f"; {measured:.1f} s of CPU time measured"),
             "stage_seconds": {"score": t_score, "select": t_select, "gather": t_gather, "attention": t_attn}}
 
 
