@@ -139,3 +139,25 @@ def test_backward_zero_upstream_gradient():
     _, _, grads = _run(binding, q, k, v, np.zeros_like(dout), pos, s, gain, 1.0, True)
     for t in grads:
         assert torch.count_nonzero(t.float()) == 0
+
+
+def test_backward_without_positions():
+    """pos = NULL means pos = row index (the unpruned layout), also in the backward."""
+    binding = require_gpu()
+    import torch
+    m, hq, hkv, d, tau = 300, 8, 4, 128, 0.9
+    q, k, v, dout, _, s, gain = _case_inputs(m, hq, hkv, d, False, seed=21)
+    qt, kt, vt, dot = (binding.to_device(a, "bf16") for a in (q, k, v, dout))
+    st, gt = torch.from_numpy(s).cuda(), torch.from_numpy(gain).cuda()
+    out, lse = binding.tg_gated_attention_lse(qt, kt, vt, None, st, gt, tau)
+    dq, dk, dv, ds, dg, dtau = binding.tg_gated_attention_backward(qt, kt, vt, None, st, gt, tau, out, lse, dot)
+    torch.cuda.synchronize()
+    f64 = lambda a: inputs.to_f64(a, "bf16")
+    rdq, rdk, rdv, rds, rdg, rdtau, mag = oracle.gated_attention_backward(
+        f64(q), f64(k), f64(v), np.arange(m), s, gain, tau, f64(dout), magnitudes=True)
+    _check_tensor("dq", host_f64(dq), rdq)
+    _check_tensor("dk", host_f64(dk), rdk)
+    _check_tensor("dv", host_f64(dv), rdv)
+    _check_tensor("ds_kept", host_f64(ds), rds)
+    assert np.all(np.abs(host_f64(dg) - rdg) <= 2e-2 * mag["dgain"] + 1e-4)
+    assert abs(float(host_f64(dtau)[0]) - rdtau) <= 2e-2 * mag["dtau"] + 1e-4
