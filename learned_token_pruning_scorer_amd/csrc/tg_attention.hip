@@ -39,6 +39,10 @@
 //  * operand reads are issued ahead of the work that waits on them: the first two
 //    k-steps' K operands before the next tile's DMA, the first d tile's V^T
 //    operands before the softmax;
+//  * a wave raises its issue priority (s_setprio) for the vector phase of a tile (mask,
+//    max, exponentials, packing) and drops it for the MFMA phases, so that of the two
+//    waves sharing a SIMD the one in its softmax goes first while the other's MFMAs run
+//    (about 5% on the 128k workload);
 //  * P^T stays in registers as the B operand of O^T = V^T . P^T; its row sums come
 //    from v_dot2_f32_bf16 on the packed bf16 P that the MFMA consumes.  The V^T
 //    operand is read from the [key][d] tile with ds_read_b64_tr_b16: each 16-lane
@@ -237,6 +241,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
+    __builtin_amdgcn_s_setprio(0);   // MFMA phase: yield issue slots to a wave in its softmax
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
@@ -258,6 +263,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
       const u32x4 e = {half == 0 ? hh : 0u, half == 0 ? ll : 0u, half == 0 ? 0x3f80u : 0u, 0u};   // 1.0 at k = 4
       sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, e), qext, sacc[kt], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(2);   // vector phase (mask, max, exp, pack) goes first
     if ((kb + kBN - 1 > q0) || (kb + kBN > m)) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -318,6 +324,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
       }
       pf[s2] = __builtin_bit_cast(bf16x8, w);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
       const u32x4 a4 = {vpre[s2][0][0], vpre[s2][0][1], vpre[s2][1][0], vpre[s2][1][1]};
