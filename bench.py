@@ -262,7 +262,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the multi-GPU design is described in DESIGN.md, not built)", file=sys.stderr)
+              "(the multi-GPU design is documented, not built)", file=sys.stderr)
         return 2
     import torch
     from learned_token_pruning_scorer_amd import binding

@@ -52,7 +52,7 @@ extern "C" {
 /* status codes */
 #define TG_OK              0
 #define TG_ERR_INVALID_ARG 1   /* null pointer, negative size, bad span, bad stride ... */
-#define TG_ERR_UNSUPPORTED 2   /* a shape or alignment this build has no kernel for */
+#define TG_ERR_UNSUPPORTED 2   /* a shape or alignment this library has no kernel for */
 #define TG_ERR_WORKSPACE   3   /* workspace too small */
 #define TG_ERR_HIP         4   /* the HIP runtime reported an error at launch */
 

@@ -7,7 +7,7 @@ extern "C" const char* tg_status_string(tg_status status) {
   switch (status) {
     case TG_OK: return "TG_OK";
     case TG_ERR_INVALID_ARG: return "TG_ERR_INVALID_ARG: invalid argument";
-    case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED: shape or alignment not supported by this build";
+    case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED: shape or alignment not supported by this library";
     case TG_ERR_WORKSPACE: return "TG_ERR_WORKSPACE: workspace too small";
     case TG_ERR_HIP: return "TG_ERR_HIP: HIP runtime error at launch";
     default: return "unknown tg_status";

@@ -16,7 +16,7 @@ Sources (pages are cited by site and title; sections by their headings):
 
 The pages give the method in words only.  The formula of the gated attention
 logit, q.k / (sqrt(d) tau) + g_h s_j under a causal mask on original positions,
-is the specification this build adopts for those words.  Readings taken where
+is the specification adopted here for those words.  Readings taken where
 the pages are silent are listed with each function.
 
 Parity status: every function here is pinned by CPU tests against library
