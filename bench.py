@@ -46,6 +46,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-score-rows", type=int, default=131072)
     ap.add_argument("--cpu-attn-rows", type=int, default=0, help="query rows of the CPU attention sample (0 = all)")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 64k budget sweep against unpruned attention")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the timings of the attention backward and the multi-budget / random selectors")
     ap.add_argument("--profile-steps", type=int, default=0,
@@ -71,12 +72,14 @@ def algorithmic(w, k):
 class Path:
     """Device-resident inputs and preallocated outputs of one workload."""
 
-    def __init__(self, name, binding, torch):
+    def __init__(self, name, binding, torch, k=None, gi=None, full_qkv=None):
+        """gi: the workload's gate inputs if already generated; full_qkv: device Q/K/V of every
+        prompt position (workloads that draw them per position), gathered here by the kept rows."""
         from learned_token_pruning_scorer_amd import configs, inputs
         self.b, self.torch = binding, torch
         self.w = w = configs.WORKLOADS[name]
-        self.k = w.budgets[0] if len(w.budgets) == 1 else w.budgets[-1]
-        self.gi = gi = inputs.gate_inputs(w)
+        self.k = k if k is not None else (w.budgets[0] if len(w.budgets) == 1 else w.budgets[-1])
+        self.gi = gi = gi if gi is not None else inputs.gate_inputs(w)
         dev = "cuda"
         self.x = binding.to_device(gi.x, w.dtype, dev)
         self.w1 = binding.to_device(gi.w1, w.dtype, dev)
@@ -92,12 +95,18 @@ class Path:
         binding.tg_gate_score(self.x, self.w1, self.w2, self.b1, gi.b2, out=self.scores)
         binding.tg_select_topk(self.scores, w.doc_begin, w.doc_end, self.k, out=self.kept, workspace=self.ws)
         torch.cuda.synchronize()
-        ai = inputs.attention_inputs(w, self.kept.cpu().numpy())
-        self.q = binding.to_device(ai.q, w.dtype, dev)
-        self.kk = binding.to_device(ai.k, w.dtype, dev)
-        self.v = binding.to_device(ai.v, w.dtype, dev)
-        self.gain = torch.from_numpy(ai.gain).to(dev)
-        self.tau = ai.tau
+        if full_qkv is not None:
+            idx = self.kept.long()
+            self.q, self.kk, self.v = (t.index_select(0, idx).contiguous() for t in full_qkv)
+            self.gain = torch.from_numpy(inputs.gains(w)).to(dev)
+            self.tau = w.tau
+        else:
+            ai = inputs.attention_inputs(w, self.kept.cpu().numpy())
+            self.q = binding.to_device(ai.q, w.dtype, dev)
+            self.kk = binding.to_device(ai.k, w.dtype, dev)
+            self.v = binding.to_device(ai.v, w.dtype, dev)
+            self.gain = torch.from_numpy(ai.gain).to(dev)
+            self.tau = ai.tau
         self.o = torch.empty_like(self.q)
 
     def step(self, ev=None):
@@ -199,6 +208,25 @@ def next_rows(path, reps):
     res["qkv_rope"] = {"us": us, "tflops": flops / (us * 1e-6) / 1e12,
                        "frac_mfma_peak": flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, "flops": flops}
     del wq, qo, kc, vc, pc, qws
+    # the key bias's cost: the same attention with s_kept = gain = NULL
+    us_on = _event_time_us(torch, lambda: b.tg_gated_attention(path.q, path.kk, path.v, path.kept, path.sk, path.gain,
+                                                                path.tau, out=path.o), reps)
+    us_off = _event_time_us(torch, lambda: b.tg_gated_attention(path.q, path.kk, path.v, path.kept, None, None,
+                                                                 path.tau, out=path.o), reps)
+    res["attention_bias_cost"] = {"us_bias_on": us_on, "us_bias_off": us_off, "ratio": us_on / us_off}
+    # one GPU's share in the head-parallel design over 8 GPUs: one K/V head and its query heads
+    group = w.n_q_heads // w.n_kv_heads
+    qs = path.q[:, :group].contiguous()
+    ks_, vs_ = path.kk[:, :1].contiguous(), path.v[:, :1].contiguous()
+    gs = path.gain[:group].contiguous()
+    os_ = torch.empty_like(qs)
+    us = _event_time_us(torch, lambda: b.tg_gated_attention(qs, ks_, vs_, path.kept, path.sk, gs, path.tau, out=os_),
+                        reps)
+    flops = 4.0 * w.head_dim * group * path.m * (path.m + 1) / 2
+    res["attention_head_shard"] = {"n_q_heads": group, "n_kv_heads": 1, "m": path.m, "us": us,
+                                   "tflops": flops / (us * 1e-6) / 1e12,
+                                   "frac_mfma_peak": flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+    del qs, ks_, vs_, gs, os_
     kept_r = torch.empty(path.m, dtype=torch.int32, device="cuda")
     us = _event_time_us(torch, lambda: b.tg_select_random(w.n, w.doc_begin, w.doc_end, path.k, 12345,
                                                           out=kept_r, workspace=path.ws), reps)
@@ -206,6 +234,49 @@ def next_rows(path, reps):
     del dout, out, lse, ws
     torch.cuda.empty_cache()
     return res
+
+
+def sweep64k(binding, torch, steps, warmup):
+    """Budget reuse at 64k: the whole path at each budget against unpruned causal attention
+    over all N rows (bias off, tau = 1), the comparison the pruning is for."""
+    from learned_token_pruning_scorer_amd import configs, inputs
+    w = configs.WORKLOADS["sweep64k"]
+    out = {"workload": w.name, "n": w.n, "points": []}
+    gi = inputs.gate_inputs(w)
+    ai = inputs.attention_inputs(w, np.arange(w.n))   # Q/K/V of every position (the unpruned run's)
+    full = tuple(binding.to_device(a, w.dtype, "cuda") for a in (ai.q, ai.k, ai.v))
+    del ai
+    for k in w.budgets:
+        p = Path(w.name, binding, torch, k=k, gi=gi, full_qkv=full)
+        sec, st, _ = p.timed(steps, warmup)
+        out["points"].append({"k": k, "m": p.m, "ms_per_step": sec * 1e3,
+                              "stage_us_mean": {"score": st[0], "select": st[1], "gather": st[2], "attention": st[3]}})
+        del p
+        torch.cuda.empty_cache()
+    q, k, v = full
+    o = torch.empty_like(q)
+    reps = max(3, steps // 4)
+    us = _event_time_us(torch, lambda: binding.tg_gated_attention(q, k, v, None, None, None, 1.0, out=o), reps,
+                        warmup=2)
+    flops = 4.0 * w.head_dim * w.n_q_heads * w.n * (w.n + 1) / 2
+    out["unpruned"] = {"m": w.n, "ms": us / 1e3, "tflops": flops / (us * 1e-6) / 1e12,
+                       "frac_mfma_peak": flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
+    for pt in out["points"]:
+        pt["time_ratio_vs_unpruned"] = (us / 1e3) / pt["ms_per_step"]
+    del q, k, v, o, full
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(name, score_rows, attn_rows):
@@ -249,7 +320,7 @@ def cpu_baseline(name, score_rows, attn_rows):
     t_attn = t_attn_sample * (work_all / work_sample)
     total = t_score + t_select + t_gather + t_attn
     measured = t_score * (len(rows) / w.n) + t_select + t_gather + t_attn_sample
-    return {"value": w.n / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": w.n / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": (f"{name}: gate score on {len(rows)} of {w.n} rows, full select and gather, "
                        f"attention on {len(arows)} of {m} query rows"
                        + ("" if len(rows) == w.n and len(arows) == m else
@@ -311,6 +382,11 @@ def main():
         print("[bench] timing the backward and the selector variants", file=sys.stderr, flush=True)
         nxt = next_rows(path, max(5, args.steps // 2))
 
+    sweep = None
+    if not args.no_sweep:
+        print("[bench] 64k budget sweep against unpruned attention", file=sys.stderr, flush=True)
+        sweep = sweep64k(binding, torch, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -347,6 +423,7 @@ def main():
         },
         "also": also,
         "next_rows": nxt,
+        "sweep64k": sweep,
     }
     print(json.dumps(out))
     return 0
