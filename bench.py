@@ -2,8 +2,9 @@
 """Throughput of the TokenGate gated-prefill hot path on one MI355X.
 
 One step = the whole path over one prompt already resident in HBM:
-    tg_gate_score (N rows) -> tg_select_topk -> tg_gather_kept -> tg_gated_attention (M rows)
-`value` = prompt tokens per second = N / (wall time of one step), K steps timed
+    tg_gate_score (N rows) -> tg_select_topk -> tg_gather_kept -> tg_gated_attention_split (M rows)
+(the gated attention with the library's own key-split plan: at long contexts it does not
+split and is the plain tg_gated_attention kernel).  `value` = prompt tokens per second = N / (wall time of one step), K steps timed
 back-to-back between two device synchronisations.  Per-stage times come from
 HIP events recorded on the launch stream inside the same timed steps.
 
@@ -108,6 +109,16 @@ class Path:
             self.gain = torch.from_numpy(ai.gain).to(dev)
             self.tau = ai.tau
         self.o = torch.empty_like(self.q)
+        hq, hkv, d = self.q.shape[1], self.kk.shape[1], self.q.shape[2]
+        self.attn_ws_bytes = binding.tg_gated_attention_split_workspace_bytes(m, hq, hkv, d, 0)
+        self.attn_ws = torch.empty(max(256, self.attn_ws_bytes), dtype=torch.uint8, device=dev)
+
+    def attention(self, out=None, s_kept="kept", gain="kept", tau=None):
+        s_kept = self.sk if s_kept == "kept" else s_kept
+        gain = self.gain if gain == "kept" else gain
+        self.b.tg_gated_attention_split(self.q, self.kk, self.v, self.kept, s_kept, gain,
+                                        self.tau if tau is None else tau, out=self.o if out is None else out,
+                                        workspace=self.attn_ws)
 
     def step(self, ev=None):
         b, w = self.b, self.w
@@ -118,7 +129,7 @@ class Path:
         if ev: ev[2].record()
         b.tg_gather_kept(self.x, self.kept, self.scores, out=self.xk, s_out=self.sk)
         if ev: ev[3].record()
-        b.tg_gated_attention(self.q, self.kk, self.v, self.kept, self.sk, self.gain, self.tau, out=self.o)
+        self.attention()
         if ev: ev[4].record()
 
     def timed(self, steps, warmup):
@@ -209,10 +220,8 @@ def next_rows(path, reps):
                        "frac_mfma_peak": flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, "flops": flops}
     del wq, qo, kc, vc, pc, qws
     # the key bias's cost: the same attention with s_kept = gain = NULL
-    us_on = _event_time_us(torch, lambda: b.tg_gated_attention(path.q, path.kk, path.v, path.kept, path.sk, path.gain,
-                                                                path.tau, out=path.o), reps)
-    us_off = _event_time_us(torch, lambda: b.tg_gated_attention(path.q, path.kk, path.v, path.kept, None, None,
-                                                                 path.tau, out=path.o), reps)
+    us_on = _event_time_us(torch, lambda: path.attention(), reps)
+    us_off = _event_time_us(torch, lambda: path.attention(s_kept=None, gain=None), reps)
     res["attention_bias_cost"] = {"us_bias_on": us_on, "us_bias_off": us_off, "ratio": us_on / us_off}
     # one GPU's share in the head-parallel design over 8 GPUs: one K/V head and its query heads
     group = w.n_q_heads // w.n_kv_heads
@@ -220,13 +229,18 @@ def next_rows(path, reps):
     ks_, vs_ = path.kk[:, :1].contiguous(), path.v[:, :1].contiguous()
     gs = path.gain[:group].contiguous()
     os_ = torch.empty_like(qs)
-    us = _event_time_us(torch, lambda: b.tg_gated_attention(qs, ks_, vs_, path.kept, path.sk, gs, path.tau, out=os_),
-                        reps)
+    sws = torch.empty(max(256, b.tg_gated_attention_split_workspace_bytes(path.m, group, 1, w.head_dim, 0)),
+                      dtype=torch.uint8, device="cuda")
+    us_plain = _event_time_us(torch, lambda: b.tg_gated_attention(qs, ks_, vs_, path.kept, path.sk, gs, path.tau,
+                                                                  out=os_), reps)
+    us = _event_time_us(torch, lambda: b.tg_gated_attention_split(qs, ks_, vs_, path.kept, path.sk, gs, path.tau,
+                                                                  out=os_, workspace=sws), reps)
     flops = 4.0 * w.head_dim * group * path.m * (path.m + 1) / 2
     res["attention_head_shard"] = {"n_q_heads": group, "n_kv_heads": 1, "m": path.m, "us": us,
+                                   "us_without_key_split": us_plain,
                                    "tflops": flops / (us * 1e-6) / 1e12,
                                    "frac_mfma_peak": flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
-    del qs, ks_, vs_, gs, os_
+    del qs, ks_, vs_, gs, os_, sws
     kept_r = torch.empty(path.m, dtype=torch.int32, device="cuda")
     us = _event_time_us(torch, lambda: b.tg_select_random(w.n, w.doc_begin, w.doc_end, path.k, 12345,
                                                           out=kept_r, workspace=path.ws), reps)
@@ -256,14 +270,17 @@ def sweep64k(binding, torch, steps, warmup):
     q, k, v = full
     o = torch.empty_like(q)
     reps = max(3, steps // 4)
-    us = _event_time_us(torch, lambda: binding.tg_gated_attention(q, k, v, None, None, None, 1.0, out=o), reps,
-                        warmup=2)
+    ws = torch.empty(max(256, binding.tg_gated_attention_split_workspace_bytes(w.n, w.n_q_heads, w.n_kv_heads,
+                                                                               w.head_dim, 0)),
+                     dtype=torch.uint8, device="cuda")
+    us = _event_time_us(torch, lambda: binding.tg_gated_attention_split(q, k, v, None, None, None, 1.0, out=o,
+                                                                        workspace=ws), reps, warmup=2)
     flops = 4.0 * w.head_dim * w.n_q_heads * w.n * (w.n + 1) / 2
     out["unpruned"] = {"m": w.n, "ms": us / 1e3, "tflops": flops / (us * 1e-6) / 1e12,
                        "frac_mfma_peak": flops / (us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS}
     for pt in out["points"]:
         pt["time_ratio_vs_unpruned"] = (us / 1e3) / pt["ms_per_step"]
-    del q, k, v, o, full
+    del q, k, v, o, full, ws
     torch.cuda.empty_cache()
     return out
 

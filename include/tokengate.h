@@ -192,6 +192,9 @@ tg_status tg_gather_kept(int32_t dtype, int64_t n, int32_t d_model, const void* 
  * q, k, v, s_kept and gain must be finite (NaN inputs give undefined output).
  * Supported: head_dim in {64, 128}; n_q_heads % n_kv_heads == 0; q, k, v, out
  * 16-byte aligned.  m = 0 is a no-op.
+ * Launch (bf16): up to 768 workgroups of query tiles (a few thousand kept rows), each
+ * workgroup walks its keys with two groups of waves and combines their softmax states
+ * (tg_gated_attention_split's key groups); beyond, one group.
  */
 tg_status tg_gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
                              int32_t head_dim, const void* q, const void* k, const void* v,
@@ -208,6 +211,48 @@ tg_status tg_gated_attention_lse(int32_t dtype, int64_t m, int32_t n_q_heads, in
                                  int32_t head_dim, const void* q, const void* k, const void* v,
                                  const int32_t* pos, const float* s_kept, const float* gain, float tau,
                                  void* out, float* lse, void* stream);
+
+/*
+ * tg_gated_attention_split -- tg_gated_attention (the same logits and mask: aiproducthub.cn,
+ * section 事件详情; aisight.pl, section "Jak to dziala") with the library's launch plan for
+ * few kept rows or few heads.  Without it, the query tile holding the last rows walks every
+ * key before it in sequence, so at a few thousand kept rows the launch is as long as that
+ * one walk while most of the GPU idles.  Two remedies, chosen by split_tiles:
+ *   - key groups: each workgroup runs two groups of waves that walk alternate key tiles
+ *     (64 keys each) of its query tile and combine their softmax states in LDS at the end
+ *     (no workspace);
+ *   - runs: each query tile's key tiles are cut into runs of split_tiles, walked by
+ *     different workgroups; every run writes its partial softmax state to the workspace
+ *     (its normalised output row Y_j = O_j / l_j in float16, its running max m_j and row
+ *     sum l_j in float32) and a second kernel combines the runs of a row: w_j = 2^(m_j - M)
+ *     l_j with M = max m_j, out = sum w_j Y_j / sum w_j, in run order (deterministic).
+ *     Query tiles with one run are written directly.  The float16 rows add at most 2^-11
+ *     relative rounding to the output and require |v| < 65504 (the largest float16) where
+ *     runs occur.
+ *   split_tiles  0: chosen by the library: with at most 768 workgroups of query tiles and
+ *                at least 4 head slots each, key groups; with fewer head slots, runs of
+ *                max(8, ceil(total key-tile work / 256)) tiles (key groups if that is not
+ *                shorter than the longest walk); beyond 768 workgroups (long contexts)
+ *                neither, i.e. the tg_gated_attention kernel itself.
+ *                < 0: no runs (key groups up to 768 workgroups, as tg_gated_attention does).
+ *                > 0: runs of split_tiles key tiles, one key group (when that leaves one
+ *                run per query tile: as < 0).
+ *   lse          NULL, or [m, n_q_heads] float32 as in tg_gated_attention_lse.
+ *   workspace    device, 256-byte aligned, at least
+ *                tg_gated_attention_split_workspace_bytes(m, n_q_heads, n_kv_heads, head_dim,
+ *                split_tiles) bytes (0 when that plan has no runs; the pointer may then be
+ *                NULL).  Contents on entry are ignored; no zero-fill needed.
+ * bf16 only; float32 runs the plain float32 kernel and ignores split_tiles and the workspace.
+ * Other arguments, precision and errors as tg_gated_attention; TG_ERR_WORKSPACE if the
+ * workspace is smaller than the plan needs.
+ */
+size_t tg_gated_attention_split_workspace_bytes(int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                                                int32_t head_dim, int32_t split_tiles);
+tg_status tg_gated_attention_split(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, const void* q, const void* k, const void* v,
+                                   const int32_t* pos, const float* s_kept, const float* gain, float tau,
+                                   void* out, float* lse, int32_t split_tiles, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * tg_gated_attention_backward -- gradient of the token-gated attention: the path by which

@@ -60,6 +60,11 @@ _lib.tg_gated_attention.argtypes = [_i32, _i64, _i32, _i32, _i32, _p, _p, _p, _p
 
 _lib.tg_gated_attention_lse.restype = _i32
 _lib.tg_gated_attention_lse.argtypes = [_i32, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _f32, _p, _p, _p]
+_lib.tg_gated_attention_split_workspace_bytes.restype = _sz
+_lib.tg_gated_attention_split_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32, _i32]
+_lib.tg_gated_attention_split.restype = _i32
+_lib.tg_gated_attention_split.argtypes = [_i32, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _f32, _p, _p, _i32,
+                                          _p, _sz, _p]
 _lib.tg_gated_attention_backward_workspace_bytes.restype = _sz
 _lib.tg_gated_attention_backward_workspace_bytes.argtypes = [_i64, _i32, _i32, _i32]
 _lib.tg_gated_attention_backward.restype = _i32
@@ -320,6 +325,32 @@ def tg_gated_attention_lse(q, k, v, pos=None, s_kept=None, gain=None, tau: float
         _dtype_code(q), m, hq, k.shape[1], d, _ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(s_kept), _ptr(gain),
         float(tau), _ptr(out), _ptr(lse), _stream(dev, stream)))
     return out, lse
+
+
+def tg_gated_attention_split_workspace_bytes(m: int, n_q_heads: int, n_kv_heads: int, head_dim: int,
+                                             split_tiles: int = 0) -> int:
+    return int(_lib.tg_gated_attention_split_workspace_bytes(m, n_q_heads, n_kv_heads, head_dim, split_tiles))
+
+
+def tg_gated_attention_split(q, k, v, pos=None, s_kept=None, gain=None, tau: float = 1.0, out=None, lse=None,
+                             split_tiles: int = 0, workspace=None, stream=None):
+    """tg_gated_attention with long query tiles' keys split over workgroups and merged;
+    `lse` (a [m, Hq] float32 tensor) is filled when given.  -> out"""
+    dev = _on_gpu(q, k, v, pos, s_kept, gain, out, lse, workspace)
+    _check_attention_args(q, k, v, pos, s_kept, gain)
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    need = tg_gated_attention_split_workspace_bytes(m, hq, hkv, d, split_tiles)
+    ws = workspace
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check("tg_gated_attention_split", _lib.tg_gated_attention_split(
+        _dtype_code(q), m, hq, hkv, d, _ptr(q), _ptr(k), _ptr(v), _ptr(pos), _ptr(s_kept), _ptr(gain),
+        float(tau), _ptr(out), _ptr(lse), int(split_tiles), _ptr(ws), ws.numel() if ws is not None else 0,
+        _stream(dev, stream)))
+    return out
 
 
 def tg_gated_attention_backward(q, k, v, pos, s_kept, gain, tau, out, lse, dout, workspace=None, stream=None):

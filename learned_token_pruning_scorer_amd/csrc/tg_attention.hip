@@ -51,6 +51,7 @@
 //    first), and consecutive workgroup ids map to different key/value heads, which
 //    the dispatcher spreads round-robin over the 8 XCDs, so each XCD's L2 holds the
 //    K/V of one head.
+#include <algorithm>
 #include <type_traits>
 
 #include "tg_common.h"
@@ -106,20 +107,37 @@ struct AttnCfg {
   static constexpr int K0 = 0, V0 = 2 * TILE, SB = 4 * TILE, PB = SB + 2 * kBN * 4, BYTES = PB + 2 * kBN * 4;
 };
 
-template <int D, int HPW, bool BIAS>
-__global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
+// Key split: query tile qt's key tiles are cut into runs of `tiles`; run j (grid y) walks
+// tiles [j tiles, (j + 1) tiles).  Query tiles with more than one run (qt >= qt0) write
+// partial states: part_o [qt - qt0][j][row in tile][head][D], the run's normalised output
+// row O_j / l_j in float16, and part_ml (same index) = [m_j, l_j] in float32; tiles = 0
+// means no split.
+struct AttnSplit {
+  int tiles, qt0, jmax;
+  _Float16* part_o;
+  float* part_ml;
+};
+
+// KS key groups per workgroup: group g (waves 4g .. 4g+3, each with its own double-buffered
+// K/V region of LDS) walks key tiles t_begin + g, t_begin + g + KS, ...; at the end the
+// groups' softmax states are combined through LDS.  RUNS: the query tile's keys are cut into
+// runs over grid y (AttnSplit).  KS = 1 without runs is the plain kernel.
+template <int D, int HPW, bool BIAS, int KS, bool RUNS>
+__global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel(
     int m, int hq, int hkv, const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ pos, const float* __restrict__ s_kept,
     const float* __restrict__ gain, float c_scale, float bias_scale, float rescale_thr,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int n_qtiles) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int n_qtiles, AttnSplit sp) {
   using C = AttnCfg<D, HPW>;
   using S = TileSwz<D>;
-  __shared__ __attribute__((aligned(16))) char lds[C::BYTES];
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)lds;
+  __shared__ __attribute__((aligned(16))) char lds_all[C::BYTES * KS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6) % kAttnWaves;
+  const int grp = KS == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6) / kAttnWaves;
   const int half = lane >> 5, l32 = lane & 31;
+  char* const lds = lds_all + grp * C::BYTES;   // this key group's buffers
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t*)lds;
 
   const int group = hq / hkv;
   const int slots_per_kv = group / HPW;
@@ -134,31 +152,17 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
   const bool wave_live = q0 < m;
   const int wave_last = min(m - 1, q0 + 31);
 
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    if (row < m) {
-      const bf16x8 raw = *reinterpret_cast<const bf16x8*>(q + ((int64_t)row * hq + head) * D + 16 * s + 8 * half);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<__bf16>(static_cast<float>(raw[e]) * c_scale);
-    } else {
-      qf[s] = bf16x8{};
-    }
+  // key tiles this workgroup walks: all of the query tile's, or one split of them
+  const int rows_end = min(m, (qt + 1) * C::ROWS);
+  const int n_tiles = (rows_end + kBN - 1) / kBN;
+  int t_begin = 0, t_end = n_tiles;
+  bool to_part = false;
+  if (RUNS) {
+    t_begin = blockIdx.y * sp.tiles;
+    if (t_begin >= n_tiles) return;   // this query tile has fewer splits (uniform over the workgroup)
+    t_end = min(n_tiles, t_begin + sp.tiles);
+    to_part = n_tiles > sp.tiles;
   }
-  const int32_t qpos = row < m ? (pos ? pos[row] : row) : INT32_MAX;
-  // extra k-step, B operand (lane half 0): [cG_hi, cG_lo, cG_hi, cG_lo, -m, 0, 0, 0] with
-  // G = gain sqrt(d) tau (so c G s = gain s in base-2 logit units) and m the running max
-  __bf16 cg_hi = static_cast<__bf16>(0.f), cg_lo = static_cast<__bf16>(0.f);
-  if (BIAS) {
-    const float cG = gain[head] * bias_scale * c_scale;
-    cg_hi = static_cast<__bf16>(cG);
-    cg_lo = static_cast<__bf16>(cG - static_cast<float>(cg_hi));
-  }
-  auto make_qext = [&](float mrun) {
-    bf16x8 e = bf16x8{};
-    if (half == 0) { e[0] = cg_hi; e[1] = cg_lo; e[2] = cg_hi; e[3] = cg_lo; e[4] = static_cast<__bf16>(-mrun); }
-    return e;
-  };
 
   // ---- DMA: per-lane byte offsets relative to the tile's first key (constant across tiles) ----
   const int64_t key_stride = (int64_t)hkv * D * 2;   // bytes between consecutive keys
@@ -199,6 +203,35 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
       else reinterpret_cast<int32_t*>(lds + C::PB + buf * kBN * 4)[lane] = min(kb + lane, m - 1);
     }
   };
+  // the first K/V tile is in flight while Q is loaded and scaled
+  if (t_begin + grp < t_end) issue_tile(t_begin + grp, 0);
+
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    if (row < m) {
+      const bf16x8 raw = *reinterpret_cast<const bf16x8*>(q + ((int64_t)row * hq + head) * D + 16 * s + 8 * half);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<__bf16>(static_cast<float>(raw[e]) * c_scale);
+    } else {
+      qf[s] = bf16x8{};
+    }
+  }
+  const int32_t qpos = row < m ? (pos ? pos[row] : row) : INT32_MAX;
+  // extra k-step, B operand (lane half 0): [cG_hi, cG_lo, cG_hi, cG_lo, -m, 0, 0, 0] with
+  // G = gain sqrt(d) tau (so c G s = gain s in base-2 logit units) and m the running max
+  __bf16 cg_hi = static_cast<__bf16>(0.f), cg_lo = static_cast<__bf16>(0.f);
+  if (BIAS) {
+    const float cG = gain[head] * bias_scale * c_scale;
+    cg_hi = static_cast<__bf16>(cG);
+    cg_lo = static_cast<__bf16>(cG - static_cast<float>(cg_hi));
+  }
+  auto make_qext = [&](float mrun) {
+    bf16x8 e = bf16x8{};
+    if (half == 0) { e[0] = cg_hi; e[1] = cg_lo; e[2] = cg_hi; e[3] = cg_lo; e[4] = static_cast<__bf16>(-mrun); }
+    return e;
+  };
+
 
   // ---- LDS operand addresses (bytes, buffer 0); other buffers/steps are immediate offsets ----
   uint32_t ka[D / 16];   // K A-operand: row l32 (+32 kt), chunk (2s + half) ^ swz
@@ -222,10 +255,14 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
   float m_run = 0.f, l_run = 0.f, l_run2 = 0.f;   // m_run: bf16-exact running max (base-2 units)
   bf16x8 qext = make_qext(0.f);
 
-  const int rows_end = min(m, (qt + 1) * C::ROWS);
-  const int n_tiles = (rows_end + kBN - 1) / kBN;
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+  // this group's tiles: tg0 + KS j for j = 0, 1, ... below t_end; every group runs the
+  // same number of iterations (and barriers), skipping the tiles past the end
+  const int tg0 = t_begin + grp;
+  const int n_iter = (t_end - t_begin + KS - 1) / KS;
+  auto tt = [&](int j) { return tg0 + KS * j; };
 
   constexpr int KPRE = 2;
   auto read_k = [&](int s, int kt, auto bufc) {
@@ -292,8 +329,8 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
             (__attribute__((address_space(3))) s16x4*)(lds + va[0] + (C::V0 + buf * C::TILE + (16 * s2 + 8 * r) * D * 2))));
     mt = pair_max(mt);   // tile max of S - m (base-2 units)
     // first tile: adopt its max; later: move the max only when exceeded by > 2^8
-    if (t == 0 || __ballot(mt > rescale_thr)) {
-      const float m_new = static_cast<float>(static_cast<__bf16>(m_run + (t == 0 ? mt : fmaxf(mt, 0.f))));
+    if (t == tg0 || __ballot(mt > rescale_thr)) {
+      const float m_new = static_cast<float>(static_cast<__bf16>(m_run + (t == tg0 ? mt : fmaxf(mt, 0.f))));
       const float delta = m_new - m_run;
       const float alpha = __builtin_amdgcn_exp2f(-delta);
       m_run = m_new;
@@ -345,35 +382,93 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
     }
   };
 
-  issue_tile(0, 0);
   wait_dma();
   __syncthreads();
-  for (int t = 0; t < n_tiles; t += 2) {
+  for (int j = 0; j < n_iter; j += 2) {
     {
       bf16x8 kp[KPRE][2];
 #pragma unroll
       for (int s = 0; s < KPRE; ++s)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) kp[s][kt] = read_k(s, kt, std::integral_constant<int, 0>{});
-      if (t + 1 < n_tiles) issue_tile(t + 1, 1);
-      tile(t, std::integral_constant<int, 0>{}, kp);
+      if (tt(j + 1) < t_end) issue_tile(tt(j + 1), 1);
+      if (KS == 1 || tt(j) < t_end) tile(tt(j), std::integral_constant<int, 0>{}, kp);
     }
     wait_dma();
     __syncthreads();
-    if (t + 1 < n_tiles) {
+    if (j + 1 < n_iter) {
       bf16x8 kp[KPRE][2];
 #pragma unroll
       for (int s = 0; s < KPRE; ++s)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) kp[s][kt] = read_k(s, kt, std::integral_constant<int, 1>{});
-      if (t + 2 < n_tiles) issue_tile(t + 2, 0);
-      tile(t + 1, std::integral_constant<int, 1>{}, kp);
+      if (tt(j + 2) < t_end) issue_tile(tt(j + 2), 0);
+      if (KS == 1 || tt(j + 1) < t_end) tile(tt(j + 1), std::integral_constant<int, 1>{}, kp);
       wait_dma();
       __syncthreads();
     }
   }
 
+  if (KS > 1) {
+    // the groups' states (running max, row sum, unnormalised O) meet in group 0; every tile
+    // is done (the loop ended on a barrier), so the K/V buffers are free.  A group that saw
+    // no key of a row has l = 0 and contributes nothing.
+    constexpr int NO = D / 32 * 16;
+    float* xs = reinterpret_cast<float*>(lds_all) + wave * ((NO + 2) * 64);
+    const float l_own = pair_sum(l_run + l_run2);
+    if (grp == 1) {
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xs[(16 * u + i) * 64 + lane] = oacc[u][i];
+      xs[NO * 64 + lane] = m_run;
+      xs[(NO + 1) * 64 + lane] = l_own;
+    }
+    __syncthreads();
+    if (grp != 0) return;
+    const float m1 = xs[NO * 64 + lane], l1 = xs[(NO + 1) * 64 + lane];
+    const float mn = l1 > 0.f ? (l_own > 0.f ? fmaxf(m_run, m1) : m1) : m_run;
+    const float a0 = l_own > 0.f ? __builtin_amdgcn_exp2f(m_run - mn) : 0.f;
+    const float a1 = l1 > 0.f ? __builtin_amdgcn_exp2f(m1 - mn) : 0.f;
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[u][i] = fmaf(a0, oacc[u][i], a1 * xs[(16 * u + i) * 64 + lane]);
+    // l_run + l_run2 is summed over the lane pair below: keep the combined row sum in one half
+    l_run = half == 0 ? fmaf(a0, l_own, a1 * l1) : 0.f;
+    l_run2 = 0.f;
+    m_run = mn;
+  }
+
   const float l_tot = pair_sum(l_run + l_run2);
+  if (RUNS && to_part) {
+    // one run of a query tile: the run's normalised output row (float16), its running max
+    // (base-2 units) and row sum go to the workspace; attn_merge_kernel combines the runs.
+    // A wave that saw no key of this run leaves l = 0, which the merge skips.
+    if (row < m) {
+      const int64_t prow =
+          ((int64_t)((qt - sp.qt0) * sp.jmax + (int)blockIdx.y) * C::ROWS + (row - qt * C::ROWS)) * hq + head;
+      _Float16* po = sp.part_o + prow * D;
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * u + 8 * g + 4 * half;
+          f16x4 o4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = static_cast<_Float16>(oacc[u][4 * g + e] * inv);
+          *reinterpret_cast<f16x4*>(po + d0) = o4;
+        }
+      if (half == 0) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        const f32x2 ml = {m_run, l_tot};
+        *reinterpret_cast<f32x2*>(sp.part_ml + prow * 2) = ml;
+      }
+    }
+    return;
+  }
   if (row < m) {
     const float inv = 1.0f / l_tot;
     // natural-log log-sum-exp of the row's logits: (m + log2(l)) in base-2 units, times ln 2
@@ -389,6 +484,124 @@ __global__ __launch_bounds__(kAttnWaves * 64, 2) void attn_bf16_kernel(
         *reinterpret_cast<u32x2*>(orow + d0) = pk;
       }
   }
+}
+
+// Combines the runs of the query tiles that were split: for a row and head with run
+// states (m_j, l_j, Y_j = O_j / l_j) (m_j in base-2 units),
+//     M = max_j m_j,  w_j = 2^(m_j - M) l_j,  out = sum_j w_j Y_j / sum_j w_j,
+// over the runs with l_j > 0, in run order.  D / 4 threads per (row, head), each owning 4
+// consecutive elements; consecutive threads cover consecutive heads of a row, so reads
+// and writes are contiguous.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(int m, int hq, int rows, int row0, AttnSplit sp,
+                                                         uint16_t* __restrict__ out, float* __restrict__ lse) {
+  constexpr int TPR = D / 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pair = gid / TPR;
+  const int d0 = 4 * (int)(gid % TPR);
+  const int row = row0 + (int)(pair / hq);
+  const int head = (int)(pair % hq);
+  if (row >= m) return;
+  const int qt = row / rows;
+  const int n_tiles = (min(m, (qt + 1) * rows) + kBN - 1) / kBN;
+  const int nj = (n_tiles + sp.tiles - 1) / sp.tiles;
+  const int64_t base = ((int64_t)(qt - sp.qt0) * sp.jmax * rows + (row - qt * rows)) * hq + head;
+  const int64_t jstride = (int64_t)rows * hq;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+  // runs are read JC at a time, every load of a group issued before any is used
+  constexpr int JC = 8;
+  float mx = -INFINITY;
+  for (int j0 = 0; j0 < nj; j0 += JC) {
+    f32x2 ml[JC];
+#pragma unroll
+    for (int c = 0; c < JC; ++c)
+      ml[c] = j0 + c < nj ? *reinterpret_cast<const f32x2*>(sp.part_ml + (base + (j0 + c) * jstride) * 2)
+                          : f32x2{0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < JC; ++c)
+      if (ml[c][1] > 0.f) mx = fmaxf(mx, ml[c][0]);
+  }
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < nj; j0 += JC) {
+    f32x2 ml[JC];
+    f16x4 y[JC];
+#pragma unroll
+    for (int c = 0; c < JC; ++c) {
+      const int64_t pr = base + (j0 + c) * jstride;
+      ml[c] = j0 + c < nj ? *reinterpret_cast<const f32x2*>(sp.part_ml + pr * 2) : f32x2{0.f, 0.f};
+      y[c] = j0 + c < nj ? *reinterpret_cast<const f16x4*>(sp.part_o + pr * D + d0) : f16x4{};
+    }
+#pragma unroll
+    for (int c = 0; c < JC; ++c) {
+      if (!(ml[c][1] > 0.f)) continue;
+      const float w = __builtin_amdgcn_exp2f(ml[c][0] - mx) * ml[c][1];
+      l += w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, static_cast<float>(y[c][e]), acc[e]);
+    }
+  }
+  const float inv = 1.0f / l;
+  const u32x2 pk = {pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  *reinterpret_cast<u32x2*>(out + ((int64_t)row * hq + head) * D + d0) = pk;
+  if (lse && d0 == 0) lse[(int64_t)row * hq + head] = (mx + __log2f(l)) * 0.69314718055994531f;
+}
+
+// Launch plan of the bf16 kernel: heads per workgroup, rows per query tile, key groups per
+// workgroup and the key split.  Measured on the workloads' shapes (Hq/Hkv = 16/8, d = 128):
+// below a few thousand kept rows the grid cannot fill the GPU with two workgroups per CU,
+// and the launch is as long as the longest query tile's walk over its keys; two key groups
+// per workgroup halve that walk with no extra traffic (-12% at 1088 rows, -19% at 2112,
+// -11% at 4160; +10% at 8256, where the grid is full).  With few head slots per query tile
+// (Hq / heads-per-workgroup < 4) even that leaves most CUs idle, and runs of key tiles spread
+// over workgroups and merged pay instead (one K/V head, 8256 rows: 169 -> 73 us).
+constexpr int kAttnKeyGroupMaxGrid = 768;
+constexpr int kAttnMaxSplitQtiles = 4096;
+
+struct AttnPlan {
+  int hpw, rows, n_qtiles, ks, tiles, qt0, jmax;
+  size_t part_o_bytes, part_ml_bytes;
+};
+
+// split_tiles: 0 = automatic, < 0 = never split, > 0 = key tiles per run (one key group).
+static AttnPlan plan_attn(int m, int hq, int hkv, int head_dim, int split_tiles) {
+  AttnPlan p{};
+  const int group = hq / hkv;
+  p.hpw = group % 4 == 0 ? 4 : (group % 2 == 0 ? 2 : 1);
+  p.rows = 32 * kAttnWaves / p.hpw;
+  p.n_qtiles = (m + p.rows - 1) / p.rows;
+  const int units = hq / p.hpw;
+  const int64_t grid = (int64_t)p.n_qtiles * units;
+  auto n_tiles = [&](int qt) { return (int)((std::min<int64_t>(m, (int64_t)(qt + 1) * p.rows) + kBN - 1) / kBN); };
+  p.ks = 1;
+  int tiles = 0;
+  if (split_tiles > 0) {
+    tiles = split_tiles;
+  } else if (grid <= kAttnKeyGroupMaxGrid) {
+    if (split_tiles < 0 || units >= 4) {
+      p.ks = 2;
+    } else if (p.n_qtiles <= kAttnMaxSplitQtiles) {
+      int64_t work = 0;
+      for (int qt = 0; qt < p.n_qtiles; ++qt) work += n_tiles(qt);
+      work *= units;
+      tiles = (int)std::max<int64_t>(8, (work + 255) / 256);
+    }
+  }
+  if (m <= 0 || tiles == 0 || p.n_qtiles > kAttnMaxSplitQtiles) return p;
+  const int nt_max = n_tiles(p.n_qtiles - 1);
+  if (tiles >= nt_max) {   // one run per query tile: as without runs
+    p.ks = grid <= kAttnKeyGroupMaxGrid ? 2 : 1;
+    return p;
+  }
+  p.tiles = tiles;
+  p.jmax = (nt_max + tiles - 1) / tiles;
+  p.qt0 = 0;
+  while (n_tiles(p.qt0) <= tiles) ++p.qt0;
+  const size_t prow = (size_t)(p.n_qtiles - p.qt0) * p.jmax * p.rows * hq;
+  p.part_o_bytes = (prow * head_dim * 2 + 255) & ~size_t(255);
+  p.part_ml_bytes = (prow * 2 * 4 + 255) & ~size_t(255);
+  return p;
 }
 
 // ---------------------------------------------------------------------------------
@@ -460,39 +673,64 @@ __global__ __launch_bounds__(kF32Rows) void attn_f32_kernel(int m, int hq, int h
   }
 }
 
+template <int D, int HPW, bool BIAS, int KS, bool RUNS>
+static void launch_attn_kernel(int m, int hq, int hkv, const void* q, const void* k, const void* v,
+                               const int32_t* pos, const float* s_kept, const float* gain, float c_scale,
+                               float bias_scale, void* out, float* lse, const AttnPlan& p, const AttnSplit& sp,
+                               dim3 grid, hipStream_t st) {
+  constexpr float kRescaleThreshold = 8.0f;   // base-2 exponent headroom of P
+  hipLaunchKernelGGL((attn_bf16_kernel<D, HPW, BIAS, KS, RUNS>), grid, dim3(kAttnWaves * 64 * KS), 0, st, m, hq, hkv,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, bias_scale, kRescaleThreshold,
+                     static_cast<uint16_t*>(out), lse, p.n_qtiles, sp);
+}
+
 template <int D, int HPW>
 static tg_status launch_attn_bf16(int m, int hq, int hkv, const void* q, const void* k, const void* v,
                                   const int32_t* pos, const float* s_kept, const float* gain, float c_scale,
-                                  float bias_scale, void* out, float* lse, hipStream_t st) {
-  using C = AttnCfg<D, HPW>;
-  const int n_qtiles = (m + C::ROWS - 1) / C::ROWS;
-  const int64_t grid = (int64_t)n_qtiles * (hq / HPW);
-  if (grid > INT32_MAX) return TG_ERR_UNSUPPORTED;
-  constexpr float kRescaleThreshold = 8.0f;   // base-2 exponent headroom of P
-  if (s_kept)
-    hipLaunchKernelGGL((attn_bf16_kernel<D, HPW, true>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0, st, m, hq,
-                       hkv, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, bias_scale, kRescaleThreshold,
-                       static_cast<uint16_t*>(out), lse, n_qtiles);
-  else
-    hipLaunchKernelGGL((attn_bf16_kernel<D, HPW, false>), dim3((unsigned)grid), dim3(kAttnWaves * 64), 0, st, m,
-                       hq, hkv, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), pos, s_kept, gain, c_scale, bias_scale, kRescaleThreshold,
-                       static_cast<uint16_t*>(out), lse, n_qtiles);
+                                  float bias_scale, void* out, float* lse, const AttnPlan& p, const AttnSplit& sp,
+                                  hipStream_t st) {
+  const int64_t gx = (int64_t)p.n_qtiles * (hq / HPW);
+  const int gy = p.tiles > 0 ? p.jmax : 1;
+  if (gx > INT32_MAX) return TG_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)gx, gy);
+  // instances: one key group (plain), one key group with runs, two key groups (no runs)
+#define TG_ATTN_LAUNCH(BIAS, KS, RUNS)                                                                         \
+  launch_attn_kernel<D, HPW, BIAS, KS, RUNS>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, lse, \
+                                             p, sp, grid, st)
+  if (s_kept) {
+    if (p.tiles > 0) TG_ATTN_LAUNCH(true, 1, true);
+    else if (p.ks == 2) TG_ATTN_LAUNCH(true, 2, false);
+    else TG_ATTN_LAUNCH(true, 1, false);
+  } else {
+    if (p.tiles > 0) TG_ATTN_LAUNCH(false, 1, true);
+    else if (p.ks == 2) TG_ATTN_LAUNCH(false, 2, false);
+    else TG_ATTN_LAUNCH(false, 1, false);
+  }
+#undef TG_ATTN_LAUNCH
   TG_CHECK_LAUNCH();
+  if (p.tiles > 0) {
+    const int row0 = p.qt0 * p.rows;
+    const int64_t threads = (int64_t)(m - row0) * hq * (D / 4);
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks > INT32_MAX) return TG_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(attn_merge_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st, m, hq, p.rows, row0, sp,
+                       static_cast<uint16_t*>(out), lse);
+    TG_CHECK_LAUNCH();
+  }
   return TG_OK;
 }
 
 template <int D>
 static tg_status dispatch_attn_bf16(int m, int hq, int hkv, const void* q, const void* k, const void* v,
                                     const int32_t* pos, const float* s_kept, const float* gain, float c_scale,
-                                    float bias_scale, void* out, float* lse, hipStream_t st) {
-  const int group = hq / hkv;
-  if (group % 4 == 0)
-    return launch_attn_bf16<D, 4>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, lse, st);
-  if (group % 2 == 0)
-    return launch_attn_bf16<D, 2>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, lse, st);
-  return launch_attn_bf16<D, 1>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, lse, st);
+                                    float bias_scale, void* out, float* lse, const AttnPlan& p,
+                                    const AttnSplit& sp, hipStream_t st) {
+  if (p.hpw == 4)
+    return launch_attn_bf16<D, 4>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, lse, p, sp, st);
+  if (p.hpw == 2)
+    return launch_attn_bf16<D, 2>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, lse, p, sp, st);
+  return launch_attn_bf16<D, 1>(m, hq, hkv, q, k, v, pos, s_kept, gain, c_scale, bias_scale, out, lse, p, sp, st);
 }
 
 }  // namespace tg
@@ -502,7 +740,7 @@ namespace tg {
 static tg_status gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                                  const void* q, const void* k, const void* v, const int32_t* pos,
                                  const float* s_kept, const float* gain, float tau, void* out, float* lse,
-                                 void* stream) {
+                                 int32_t split_tiles, void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != TG_F32 && dtype != TG_BF16) return TG_ERR_INVALID_ARG;
   if (m < 0 || m > INT32_MAX || n_q_heads <= 0 || n_kv_heads <= 0) return TG_ERR_INVALID_ARG;
   if (n_q_heads % n_kv_heads != 0) return TG_ERR_INVALID_ARG;
@@ -520,11 +758,19 @@ static tg_status gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, in
   const float bias_scale = static_cast<float>(std::sqrt((double)head_dim) * (double)tau);   // bias in q.k units
   const int mm = static_cast<int>(m);
   if (dtype == TG_BF16) {
+    const AttnPlan p = plan_attn(mm, n_q_heads, n_kv_heads, head_dim, split_tiles);
+    AttnSplit sp{p.tiles, p.qt0, p.jmax, nullptr, nullptr};
+    if (p.tiles > 0) {
+      if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return TG_ERR_INVALID_ARG;
+      if (workspace_bytes < p.part_o_bytes + p.part_ml_bytes) return TG_ERR_WORKSPACE;
+      sp.part_o = static_cast<_Float16*>(workspace);
+      sp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_o_bytes);
+    }
     return head_dim == 128
                ? dispatch_attn_bf16<128>(mm, n_q_heads, n_kv_heads, q, k, v, pos, s_kept, gain, c_scale,
-                                         bias_scale, out, lse, st)
+                                         bias_scale, out, lse, p, sp, st)
                : dispatch_attn_bf16<64>(mm, n_q_heads, n_kv_heads, q, k, v, pos, s_kept, gain, c_scale,
-                                        bias_scale, out, lse, st);
+                                        bias_scale, out, lse, p, sp, st);
   }
   const dim3 grid((mm + kF32Rows - 1) / kF32Rows, n_q_heads);
   if (head_dim == 128)
@@ -546,7 +792,7 @@ extern "C" tg_status tg_gated_attention(int32_t dtype, int64_t m, int32_t n_q_he
                                         const int32_t* pos, const float* s_kept, const float* gain, float tau,
                                         void* out, void* stream) {
   return tg::gated_attention(dtype, m, n_q_heads, n_kv_heads, head_dim, q, k, v, pos, s_kept, gain, tau, out,
-                             nullptr, stream);
+                             nullptr, -1, nullptr, 0, stream);
 }
 
 extern "C" tg_status tg_gated_attention_lse(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
@@ -555,5 +801,22 @@ extern "C" tg_status tg_gated_attention_lse(int32_t dtype, int64_t m, int32_t n_
                                             void* out, float* lse, void* stream) {
   if (!lse && m > 0) return TG_ERR_INVALID_ARG;
   return tg::gated_attention(dtype, m, n_q_heads, n_kv_heads, head_dim, q, k, v, pos, s_kept, gain, tau, out, lse,
-                             stream);
+                             -1, nullptr, 0, stream);
+}
+
+extern "C" size_t tg_gated_attention_split_workspace_bytes(int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                                                           int32_t head_dim, int32_t split_tiles) {
+  if (m <= 0 || m > INT32_MAX || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads != 0) return 0;
+  if (head_dim != 64 && head_dim != 128) return 0;
+  const tg::AttnPlan p = tg::plan_attn(static_cast<int>(m), n_q_heads, n_kv_heads, head_dim, split_tiles);
+  return p.part_o_bytes + p.part_ml_bytes;
+}
+
+extern "C" tg_status tg_gated_attention_split(int32_t dtype, int64_t m, int32_t n_q_heads, int32_t n_kv_heads,
+                                              int32_t head_dim, const void* q, const void* k, const void* v,
+                                              const int32_t* pos, const float* s_kept, const float* gain, float tau,
+                                              void* out, float* lse, int32_t split_tiles, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  return tg::gated_attention(dtype, m, n_q_heads, n_kv_heads, head_dim, q, k, v, pos, s_kept, gain, tau, out, lse,
+                             split_tiles, workspace, workspace_bytes, stream);
 }

@@ -43,6 +43,9 @@ def lib():
     lib.tg_select_topk_multi.argtypes = [i64, p, i64, i64, ctypes.POINTER(i64), i32, p, p, sz, p]
     lib.tg_select_random.argtypes = [i64, i64, i64, i64, ctypes.c_uint64, p, p, sz, p]
     lib.tg_gated_attention_lse.argtypes = [i32, i64, i32, i32, i32, p, p, p, p, p, p, f32, p, p, p]
+    lib.tg_gated_attention_split_workspace_bytes.restype = sz
+    lib.tg_gated_attention_split_workspace_bytes.argtypes = [i64, i32, i32, i32, i32]
+    lib.tg_gated_attention_split.argtypes = [i32, i64, i32, i32, i32, p, p, p, p, p, p, f32, p, p, i32, p, sz, p]
     lib.tg_gated_attention_backward_workspace_bytes.restype = sz
     lib.tg_gated_attention_backward_workspace_bytes.argtypes = [i64, i32, i32, i32]
     lib.tg_gated_attention_backward.argtypes = [i32, i64, i32, i32, i32, p, p, p, p, p, p, f32, p, p, p,
@@ -194,6 +197,58 @@ def test_attention_lse_and_backward_validation(lib):
     assert bwd(d=96) == TG_ERR_UNSUPPORTED
     assert bwd(dq=ctypes.c_void_p((1 << 20) + 4)) == TG_ERR_UNSUPPORTED
     assert bwd(m=0) == TG_OK
+
+
+def split_plan_bytes(m, hq, hkv, d, split_tiles):
+    """The documented launch plan's workspace, restated: query tiles of 32 * 4 / heads-per-
+    workgroup rows, key tiles of 64; runs only when split_tiles > 0, or automatically with
+    at most 768 workgroups and fewer than 4 head slots (max(8, ceil(work / 256)) tiles)."""
+    group = hq // hkv
+    hpw = 4 if group % 4 == 0 else (2 if group % 2 == 0 else 1)
+    rows = 128 // hpw
+    units = hq // hpw
+    nq = -(-m // rows)
+    nt = [-(-min(m, (qt + 1) * rows) // 64) for qt in range(nq)]
+    if split_tiles > 0:
+        tiles = split_tiles
+    elif split_tiles == 0 and nq * units <= 768 and units < 4:
+        tiles = max(8, -(-sum(nt) * units // 256))
+    else:
+        return 0
+    if tiles >= nt[-1]:
+        return 0
+    jmax = -(-nt[-1] // tiles)
+    qt0 = next(qt for qt in range(nq) if nt[qt] > tiles)
+    prow = (nq - qt0) * jmax * rows * hq
+    up = lambda b: (b + 255) // 256 * 256
+    return up(prow * d * 2) + up(prow * 2 * 4)
+
+
+def test_attention_split_plan_and_validation(lib):
+    wsb = lib.tg_gated_attention_split_workspace_bytes
+    # 16k needle workload (M = 1088, Hq/Hkv = 16/8, d = 128): 8 head slots, key groups, no runs
+    assert wsb(1088, 16, 8, 128, 0) == 0
+    assert wsb(8256, 16, 8, 128, 0) == 0            # 128k: neither
+    # runs of 3 key tiles forced: 6 runs at most, query tiles 3.. split:
+    # (17 - 3) * 6 * 64 rows * 16 heads of 128 halves + 2 floats
+    assert wsb(1088, 16, 8, 128, 3) == 86016 * 128 * 2 + 86016 * 2 * 4 == split_plan_bytes(1088, 16, 8, 128, 3)
+    # one K/V head and its two query heads at 128k (the head-parallel shard): runs of 33 tiles
+    assert wsb(8256, 2, 1, 128, 0) == split_plan_bytes(8256, 2, 1, 128, 0) > 0
+    assert wsb(1088, 16, 8, 128, -1) == 0
+    assert wsb(1088, 16, 8, 128, 17) == 0           # one run covers the longest query tile
+    for case in [(1, 4, 2, 64, 0), (300, 4, 2, 64, 1), (2112, 16, 8, 128, 0), (4160, 16, 8, 128, 0), (777, 8, 2, 64, 2),
+                 (777, 3, 1, 128, 3), (1000, 6, 6, 64, 0), (5000, 32, 8, 128, 5)]:
+        assert wsb(*case) == split_plan_bytes(*case), case
+    assert wsb(0, 4, 2, 64, 0) == 0 and wsb(100, 3, 2, 64, 0) == 0 and wsb(100, 4, 2, 96, 0) == 0
+    f = ctypes.c_float
+    need = wsb(1088, 16, 8, 128, 3)
+    call = lambda **kw: lib.tg_gated_attention_split(
+        kw.get("dt", 1), kw.get("m", 1088), 16, 8, 128, FAKE, FAKE, FAKE, None, None, None, f(1.0), FAKE, None,
+        kw.get("split", 3), kw.get("ws", FAKE), kw.get("wsb", need), None)
+    assert call(ws=None) == TG_ERR_INVALID_ARG
+    assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == TG_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == TG_ERR_WORKSPACE
+    assert call(m=0, ws=None, wsb=0) == TG_OK
 
 
 def test_qkv_rope_validation(lib):
