@@ -30,6 +30,15 @@ def _select_cases():
     cases.append(("low-bits", g.permutation(near), 0, 3000, [1, 61, 1500, 2999]))
     big = np.round(g.normal(size=300000) * 64) / 64
     cases.append(("large-ties", big, 0, 299000, [12345, 150000]))
+    cases.append(("all-equal-large", np.full(140000, 0.25), 0, 139000, [1, 70000, 138999]))
+    cases.append(("coarse-ties-large", np.round(g.normal(size=131072) * 4) / 4, 0, 131008, [8192, 60000]))
+    cases.append(("normal-131072", g.normal(size=131072), 0, 131008, [1, 8192, 131007]))
+    cases.append(("ties-32768", np.round(g.normal(size=32768) * 8) / 8, 0, 32640, [1, 4096, 32639]))
+    cases.append(("normal-16384", g.normal(size=16384), 0, 16320, [1024, 16319]))
+    cases.append(("ragged-16385", g.normal(size=16385), 3, 16385, [5, 8000]))
+    cases.append(("all-equal-20000", np.full(20000, -1.5), 100, 19900, [1, 9999, 19799]))
+    # more positions than 64 chunks hold in registers: keys are re-read in every pass
+    cases.append(("beyond-registers-140001", g.normal(size=140001), 0, 139000, [1, 4096, 100000]))
     return cases
 
 
@@ -52,8 +61,8 @@ def test_select_workspace_reuse_across_sizes():
     import torch
     g = np.random.default_rng(8)
     ws = torch.zeros(binding.tg_select_workspace_bytes(200000), dtype=torch.uint8, device="cuda")
-    for n in (200000, 3000, 77, 150000, 3000):
-        s = np.round(g.normal(size=n) * 16) / 16
+    for n, q in ((200000, 16), (3000, 16), (77, 16), (150000, 1), (3000, 16), (140000, 64), (32768, 4)):
+        s = np.round(g.normal(size=n) * q) / q
         k = int(g.integers(1, n - 10))
         kept = binding.tg_select_topk(torch.from_numpy(s.astype(np.float32)).cuda(), 5, n - 5, k, workspace=ws)
         assert np.array_equal(kept.cpu().numpy().astype(np.int64), oracle.select_topk(s, 5, n - 5, k))
