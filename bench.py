@@ -3,10 +3,12 @@
 
 One step = the whole path over one prompt already resident in HBM:
     tg_gate_score (N rows) -> tg_select_topk -> tg_gather_kept -> tg_gated_attention_split (M rows)
-(the gated attention with the library's own key-split plan: at long contexts it does not
-split and is the plain tg_gated_attention kernel).  `value` = prompt tokens per second = N / (wall time of one step), K steps timed
-back-to-back between two device synchronisations.  Per-stage times come from
-HIP events recorded on the launch stream inside the same timed steps.
+(the gated attention with the library's own launch plan: at long contexts it is the plain
+tg_gated_attention kernel).  The four launches of a step are captured once in a HIP graph
+(torch.cuda.CUDAGraph over the library's calls) and replayed: `value` = prompt tokens per
+second = N / (wall time of one step), K replays timed back-to-back between two device
+synchronisations.  Per-stage times come from HIP events recorded on the launch stream
+inside K eager steps of the same path.
 
 Prints ONE JSON line.  Inputs are seeded synthetic tensors of the workload's
 shape (no dataset, no trained weights): see learned_token_pruning_scorer_amd/inputs.py.
@@ -131,6 +133,36 @@ class Path:
         if ev: ev[3].record()
         self.attention()
         if ev: ev[4].record()
+
+    def graph(self):
+        """The step captured in a HIP graph (after warm-up launches on a side stream)."""
+        if getattr(self, "_graph", None) is None:
+            torch = self.torch
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(2):
+                    self.step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            self._graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(self._graph):
+                self.step()
+            torch.cuda.synchronize()
+        return self._graph
+
+    def timed_graph(self, steps, warmup):
+        """Wall time per step of `steps` graph replays, after `warmup` untimed ones."""
+        torch = self.torch
+        g = self.graph()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps
 
     def timed(self, steps, warmup):
         torch = self.torch
@@ -262,8 +294,9 @@ def sweep64k(binding, torch, steps, warmup):
     del ai
     for k in w.budgets:
         p = Path(w.name, binding, torch, k=k, gi=gi, full_qkv=full)
-        sec, st, _ = p.timed(steps, warmup)
-        out["points"].append({"k": k, "m": p.m, "ms_per_step": sec * 1e3,
+        sec_e, st, _ = p.timed(steps, warmup)
+        sec = p.timed_graph(steps, warmup)
+        out["points"].append({"k": k, "m": p.m, "ms_per_step": sec * 1e3, "eager_ms_per_step": sec_e * 1e3,
                               "stage_us_mean": {"score": st[0], "select": st[1], "gather": st[2], "attention": st[3]}})
         del p
         torch.cuda.empty_cache()
@@ -374,22 +407,26 @@ def main():
         print(f"[bench] profiled {args.profile_steps} steps of {args.workload}", file=sys.stderr, flush=True)
         return 0
 
-    sec, stage_mean, stage_med = path.timed(args.steps, args.warmup)
+    sec_eager, stage_mean, stage_med = path.timed(args.steps, args.warmup)
+    sec = path.timed_graph(args.steps, args.warmup)
     w = path.w
     alg = algorithmic(w, path.k)
     attn_tflops = alg["attn_flops"] / (stage_mean[3] * 1e-6) / 1e12
     sel_gather_gbs = (alg["select_bytes"] + alg["gather_bytes"]) / ((stage_mean[1] + stage_mean[2]) * 1e-6) / 1e9
     score_gbs = alg["score_bytes"] / (stage_mean[0] * 1e-6) / 1e9
     score_tflops = alg["score_flops"] / (stage_mean[0] * 1e-6) / 1e12
-    print(f"[bench] {args.workload}: {sec * 1e3:.3f} ms/step; stages us (mean) score {stage_mean[0]:.1f} "
+    print(f"[bench] {args.workload}: {sec * 1e3:.3f} ms/step (graph), {sec_eager * 1e3:.3f} eager; "
+          f"stages us (mean) score {stage_mean[0]:.1f} "
           f"select {stage_mean[1]:.1f} gather {stage_mean[2]:.1f} attention {stage_mean[3]:.1f}",
           file=sys.stderr, flush=True)
 
     also = None
     if args.also and args.also != args.workload:
         p2 = Path(args.also, binding, torch)
-        sec2, st2, _ = p2.timed(args.steps, args.warmup)
+        sec2e, st2, _ = p2.timed(args.steps, args.warmup)
+        sec2 = p2.timed_graph(args.steps, args.warmup)
         also = {"workload": args.also, "tokens_per_s": p2.w.n / sec2, "ms_per_step": sec2 * 1e3,
+                "eager_ms_per_step": sec2e * 1e3, "eager_tokens_per_s": p2.w.n / sec2e,
                 "stage_us_mean": {"score": st2[0], "select": st2[1], "gather": st2[2], "attention": st2[3]}}
         del p2
         torch.cuda.empty_cache()
@@ -417,6 +454,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": sec * 1e3,
+        "eager_ms_per_step": sec_eager * 1e3,
+        "step_launch": "HIP graph of the step's four launches, replayed; eager steps give the stage times",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -181,3 +181,71 @@ def test_path_is_deterministic():
     for a, b in zip(*outs):
         assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+@pytest.mark.parametrize("name", ["niah16k", "long128k"])
+def test_step_graph_replays_match_eager(name):
+    """The path's four launches captured in one HIP graph (as the benchmark replays them):
+    every replay, with eager work and host synchronisations between replays, reproduces the
+    eager step's scores, kept list, gathered rows and attention output bit for bit."""
+    binding = require_gpu()
+    import torch
+    w = configs.WORKLOADS[name]
+    gi = gate_inputs(name)
+    dev = "cuda"
+    k = w.budgets[0]
+    m = w.n_kept(k)
+    x = binding.to_device(gi.x, w.dtype, dev)
+    w1 = binding.to_device(gi.w1, w.dtype, dev)
+    w2 = binding.to_device(gi.w2, w.dtype, dev)
+    b1 = torch.from_numpy(gi.b1).to(dev)
+    scores = torch.empty(w.n, dtype=torch.float32, device=dev)
+    kept = torch.empty(m, dtype=torch.int32, device=dev)
+    sel_ws = torch.zeros(binding.tg_select_workspace_bytes(w.n), dtype=torch.uint8, device=dev)
+    xk = torch.empty(m, w.d_model, dtype=x.dtype, device=dev)
+    sk = torch.empty(m, dtype=torch.float32, device=dev)
+    binding.tg_gate_score(x, w1, w2, b1, gi.b2, out=scores)
+    binding.tg_select_topk(scores, w.doc_begin, w.doc_end, k, out=kept, workspace=sel_ws)
+    ai = inputs.attention_inputs(w, kept.cpu().numpy())
+    q, kk, v = (binding.to_device(a, w.dtype, dev) for a in (ai.q, ai.k, ai.v))
+    gain = torch.from_numpy(ai.gain).to(dev)
+    o = torch.empty_like(q)
+    att_ws = torch.empty(max(256, binding.tg_gated_attention_split_workspace_bytes(m, w.n_q_heads, w.n_kv_heads,
+                                                                                   w.head_dim, 0)),
+                         dtype=torch.uint8, device=dev)
+
+    def step():
+        binding.tg_gate_score(x, w1, w2, b1, gi.b2, out=scores)
+        binding.tg_select_topk(scores, w.doc_begin, w.doc_end, k, out=kept, workspace=sel_ws)
+        binding.tg_gather_kept(x, kept, scores, out=xk, s_out=sk)
+        binding.tg_gated_attention_split(q, kk, v, kept, sk, gain, ai.tau, out=o, workspace=att_ws)
+
+    outs = (scores, kept, xk, sk, o)
+    bits = lambda t: t.view(torch.uint8) if t.dtype == torch.bfloat16 else t
+    step()
+    torch.cuda.synchronize()
+    ref = [bits(t).clone() for t in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    log(f"[graph {name}] capturing the step")
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:   # eager work between replays: clobber every output
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"  replay {rep}")
+        for a, r in zip(outs, ref):
+            assert torch.equal(bits(a), r)
+        step()           # and an eager step in between
+        torch.cuda.synchronize()
+        for a, r in zip(outs, ref):
+            assert torch.equal(bits(a), r)
