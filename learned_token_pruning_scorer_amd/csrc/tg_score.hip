@@ -265,19 +265,21 @@ constexpr int kRingKC = 64;                 // k elements per stage
 constexpr int kRingRow = kRingKC * 2;       // bytes per row per stage
 __device__ __forceinline__ int ring_swz(int row) { return (row >> 1) & 7; }
 
-template <int BTW, int NS>
+// WH waves split the 256 hidden units (AT 32-unit tiles each), the other kScoreWaves / WH
+// split the tokens (BTW 32-token tiles each).
+template <int BTW, int NS, int WH_ = 2>
 struct RingTile {
-  static constexpr int H = 256, AT = 4, WH = 2, WT = kScoreWaves / WH, BT = 32 * BTW * WT;
+  static constexpr int H = 256, WH = WH_, AT = H / 32 / WH, WT = kScoreWaves / WH, BT = 32 * BTW * WT;
   static constexpr int WB = H * kRingRow, XB = BT * kRingRow, STAGE = WB + XB;
   static constexpr int WI = WB / 1024 / kScoreWaves, XI = XB / 1024 / kScoreWaves;   // DMAs per wave per stage
   static_assert(WI >= 1 && XI >= 1, "stage split over the waves");
 };
 
-template <int BTW, int NS>
+template <int BTW, int NS, int WH>
 __global__ __launch_bounds__(kScoreWaves * 64, 1) void score_ring_kernel(
     int n, int d_model, const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w1,
     const float* __restrict__ b1, const uint16_t* __restrict__ w2, float b2, float* __restrict__ scores) {
-  using T = RingTile<BTW, NS>;
+  using T = RingTile<BTW, NS, WH>;
   constexpr int H = T::H, BT = T::BT, AT = T::AT, WT = T::WT;
   __shared__ __attribute__((aligned(16))) char ring[NS * T::STAGE];
   __shared__ __attribute__((aligned(16))) float w2f[H];
@@ -407,12 +409,12 @@ __global__ __launch_bounds__(kScoreWaves * 64, 1) void score_ring_kernel(
   }
 }
 
-template <int BTW, int NS>
+template <int BTW, int NS, int WH = 2>
 static tg_status launch_score_ring(int n, int d_model, const void* x, int64_t ldx, const void* w1, const float* b1,
                                    const void* w2, float b2, float* scores, hipStream_t stream) {
-  constexpr int BT = RingTile<BTW, NS>::BT;
+  constexpr int BT = RingTile<BTW, NS, WH>::BT;
   const int grid = (n + BT - 1) / BT;
-  hipLaunchKernelGGL((score_ring_kernel<BTW, NS>), dim3(grid), dim3(kScoreWaves * 64), 0, stream, n, d_model,
+  hipLaunchKernelGGL((score_ring_kernel<BTW, NS, WH>), dim3(grid), dim3(kScoreWaves * 64), 0, stream, n, d_model,
                      static_cast<const uint16_t*>(x), ldx, static_cast<const uint16_t*>(w1), b1,
                      static_cast<const uint16_t*>(w2), b2, scores);
   TG_CHECK_LAUNCH();
@@ -444,8 +446,10 @@ extern "C" tg_status tg_gate_score(int32_t dtype, int64_t n, int32_t d_model, in
   const int nn = static_cast<int>(n);
   // d_hidden 256: DMA ring; 256-token tiles (two stages) once there are enough of them to
   // fill the chip, which halves the W1 re-reads per token, else 128-token tiles (three
-  // stages).  The row offsets of one tile must fit 32 bits.  64/128: register-staged tiles.
-  const bool big = n >= 65536;
+  // stages), and 64-token tiles (4 waves along the hidden units) below 32768 tokens, where
+  // 128-token tiles leave CUs idle.  The row offsets of one tile must fit 32 bits.
+  // 64/128: register-staged tiles.
+  const bool big = n >= 65536, small = n < 32768;
   switch (d_hidden) {
     case 64:
       return launch_score_bf16<64, 1>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
@@ -453,8 +457,9 @@ extern "C" tg_status tg_gate_score(int32_t dtype, int64_t n, int32_t d_model, in
       return launch_score_bf16<128, 1>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
     case 256:
       if ((int64_t)ldx * 2 * 256 > INT32_MAX || (int64_t)d_model * 2 * 256 > INT32_MAX) return TG_ERR_UNSUPPORTED;
-      return big ? launch_score_ring<2, 2>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st)
-                 : launch_score_ring<1, 3>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
+      if (big) return launch_score_ring<2, 2>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
+      if (small) return launch_score_ring<1, 3, 4>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
+      return launch_score_ring<1, 3>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
     default:
       return TG_ERR_UNSUPPORTED;
   }
