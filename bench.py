@@ -34,9 +34,9 @@ CALIB_BYTES = 1 << 30          # streaming copy in --profile-steps mode: reads a
 # HBM bytes per launch of the attention kernel on long128k, from rocprofv3 FETCH_SIZE and WRITE_SIZE
 # scaled by the same counters' reading of the calibration copy (profiles/long128k_hbm_counters.md).
 # Reported only while the kernel source is the one the counters were taken on.
-ATTN_TRAFFIC = {"workload": "long128k", "bytes": 116913687,
+ATTN_TRAFFIC = {"workload": "long128k", "bytes": 117230024,
                 "source": "learned_token_pruning_scorer_amd/csrc/tg_attention.hip",
-                "sha256": "a01cd440044d63909bbf28083bab0f7c42b81744cdeb0a6da5d1535ae932470d"}
+                "sha256": "a0b0fea08b84e6f455614be597e7ac3a3d9eebdf73249dffa7c4e3e56aa121e7"}
 
 
 def parse():
