@@ -164,6 +164,22 @@ class Path:
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) / steps
 
+    def timed_cold(self, reps):
+        """Median time of a replayed step with the caches flushed before it: a 1 GiB fill (outside
+        the events) evicts the L2s and the 256 MB Infinity Cache, so X comes from HBM."""
+        torch = self.torch
+        g = self.graph()
+        flush = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            flush.zero_()
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        del flush
+        return float(np.median([a.elapsed_time(b) for a, b in evs])) / 1e3
+
     def timed(self, steps, warmup):
         torch = self.torch
         for _ in range(warmup):
@@ -177,6 +193,10 @@ class Path:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs]) * 1e3   # us
+        # step period on the GPU timeline (start of one step to the start of the next), median:
+        # robust to a host hiccup, which the wall-clock mean is not
+        period = [evs[i][0].elapsed_time(evs[i + 1][0]) for i in range(steps - 1)] or [wall * 1e3]
+        self.eager_period = float(np.median(period)) / 1e3
         return wall / steps, stage.mean(axis=0), np.median(stage, axis=0)
 
 
@@ -292,14 +312,50 @@ def sweep64k(binding, torch, steps, warmup):
     ai = inputs.attention_inputs(w, np.arange(w.n))   # Q/K/V of every position (the unpruned run's)
     full = tuple(binding.to_device(a, w.dtype, "cuda") for a in (ai.q, ai.k, ai.v))
     del ai
+    x_bytes = w.n * w.d_model * 2
+
+    def window():
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats()
+        return torch.cuda.memory_allocated()
+
     for k in w.budgets:
+        # peak device bytes of the pruned path: its own tensors (X, gate weights, scores, kept list,
+        # workspaces, gathered rows, the kept rows' Q/K/V, output) allocated and one step run
+        # inside the window
+        base = window()
         p = Path(w.name, binding, torch, k=k, gi=gi, full_qkv=full)
-        sec_e, st, _ = p.timed(steps, warmup)
+        p.step()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        _, st, _ = p.timed(steps, warmup)
+        sec_e = p.eager_period
         sec = p.timed_graph(steps, warmup)
         out["points"].append({"k": k, "m": p.m, "ms_per_step": sec * 1e3, "eager_ms_per_step": sec_e * 1e3,
+                              "peak_bytes": peak,
                               "stage_us_mean": {"score": st[0], "select": st[1], "gather": st[2], "attention": st[3]}})
         del p
         torch.cuda.empty_cache()
+    # peak device bytes of the unpruned layer: X, Q/K/V of all N rows, output, run once
+    base = window()
+    xu = binding.to_device(gi.x, w.dtype, "cuda")
+    qu, ku, vu = (t.clone() for t in full)
+    ou = torch.empty_like(qu)
+    wsu = torch.empty(max(256, binding.tg_gated_attention_split_workspace_bytes(w.n, w.n_q_heads, w.n_kv_heads,
+                                                                                w.head_dim, 0)),
+                      dtype=torch.uint8, device="cuda")
+    binding.tg_gated_attention_split(qu, ku, vu, None, None, None, 1.0, out=ou, workspace=wsu)
+    torch.cuda.synchronize()
+    peak_u = torch.cuda.max_memory_allocated() - base
+    del xu, qu, ku, vu, ou, wsu
+    torch.cuda.empty_cache()
+    out["memory"] = {"unpruned_peak_bytes": peak_u, "x_bytes": x_bytes,
+                     "note": "peak device bytes allocated by each path's own tensors over one run; "
+                             "ratios with X (the gate layer's input, held by both) counted and excluded"}
+    for pt in out["points"]:
+        pt["memory_ratio_vs_unpruned"] = peak_u / pt["peak_bytes"]
+        pt["memory_ratio_vs_unpruned_excl_x"] = (peak_u - x_bytes) / (pt["peak_bytes"] - x_bytes)
     q, k, v = full
     o = torch.empty_like(q)
     reps = max(3, steps // 4)
@@ -407,8 +463,10 @@ def main():
         print(f"[bench] profiled {args.profile_steps} steps of {args.workload}", file=sys.stderr, flush=True)
         return 0
 
-    sec_eager, stage_mean, stage_med = path.timed(args.steps, args.warmup)
+    _, stage_mean, stage_med = path.timed(args.steps, args.warmup)
+    sec_eager = path.eager_period
     sec = path.timed_graph(args.steps, args.warmup)
+    sec_cold = path.timed_cold(max(5, args.steps // 2))
     w = path.w
     alg = algorithmic(w, path.k)
     attn_tflops = alg["attn_flops"] / (stage_mean[3] * 1e-6) / 1e12
@@ -423,9 +481,12 @@ def main():
     also = None
     if args.also and args.also != args.workload:
         p2 = Path(args.also, binding, torch)
-        sec2e, st2, _ = p2.timed(args.steps, args.warmup)
+        _, st2, _ = p2.timed(args.steps, args.warmup)
+        sec2e = p2.eager_period
         sec2 = p2.timed_graph(args.steps, args.warmup)
+        sec2c = p2.timed_cold(max(5, args.steps // 2))
         also = {"workload": args.also, "tokens_per_s": p2.w.n / sec2, "ms_per_step": sec2 * 1e3,
+                "cold_ms_per_step": sec2c * 1e3, "cold_tokens_per_s": p2.w.n / sec2c,
                 "eager_ms_per_step": sec2e * 1e3, "eager_tokens_per_s": p2.w.n / sec2e,
                 "stage_us_mean": {"score": st2[0], "select": st2[1], "gather": st2[2], "attention": st2[3]}}
         del p2
@@ -455,7 +516,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": sec * 1e3,
         "eager_ms_per_step": sec_eager * 1e3,
-        "step_launch": "HIP graph of the step's four launches, replayed; eager steps give the stage times",
+        "cold_ms_per_step": sec_cold * 1e3,
+        "step_launch": "HIP graph of the step's four launches, replayed back to back; eager steps give the "
+                       "stage times; cold = median replay after a 1 GiB fill that evicts L2 and the Infinity Cache",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
