@@ -34,9 +34,9 @@ CALIB_BYTES = 1 << 30          # streaming copy in --profile-steps mode: reads a
 # HBM bytes per launch of the attention kernel on long128k, from rocprofv3 FETCH_SIZE and WRITE_SIZE
 # scaled by the same counters' reading of the calibration copy (profiles/long128k_hbm_counters.md).
 # Reported only while the kernel source is the one the counters were taken on.
-ATTN_TRAFFIC = {"workload": "long128k", "bytes": 117230024,
+ATTN_TRAFFIC = {"workload": "long128k", "bytes": 116942549,
                 "source": "learned_token_pruning_scorer_amd/csrc/tg_attention.hip",
-                "sha256": "a0b0fea08b84e6f455614be597e7ac3a3d9eebdf73249dffa7c4e3e56aa121e7"}
+                "sha256": "a9bb7310298659b24399b6e8412d8d04abf8245b1739c76501eafe27c9c514e9"}
 
 
 def parse():

@@ -53,6 +53,7 @@
 //    K/V of one head.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "tg_common.h"
 
@@ -67,13 +68,26 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // does not serialise later LDS reads behind them; the kernel waits for them itself
 // (wait_dma) before the barrier that publishes a tile.  M0 (the LDS destination,
 // wave-uniform) is saved and restored around the issue; the global address is a
-// 64-bit scalar base plus a 32-bit per-lane offset.
-__device__ __forceinline__ void dma16x2(uint32_t ko, const void* kb, uint32_t km0, uint32_t vo, const void* vb,
-                                        uint32_t vm0) {
+// 64-bit scalar base plus a 32-bit per-lane offset.  dma16x2 issues a K and a V piece
+// whose LDS destinations are one wave-uniform base plus compile-time byte offsets KM and
+// VM, added into M0 inside the asm: the base is then the only LDS address the loop keeps
+// in a scalar register (precomputed destinations, one per piece and buffer, outgrow the
+// scalar file and are spilled to vector lanes, costing a v_readlane per DMA).
+template <uint32_t KM, uint32_t VM>
+__device__ __forceinline__ void dma16x2(uint32_t m0base, uint32_t ko, const void* kb, uint32_t vo, const void* vb) {
   uint32_t save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\t"
-               "s_mov_b32 m0, %4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %5, %6\n\ts_mov_b32 m0, %0"
-               : "=&s"(save) : "s"(km0), "v"(ko), "s"(kb), "s"(vm0), "v"(vo), "s"(vb) : "memory");
+  asm volatile("s_mov_b32 %0, m0\n\ts_add_u32 m0, %1, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %3, %4\n\t"
+               "s_add_u32 m0, %1, %5\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %6, %7\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "s"(m0base), "n"(KM), "v"(ko), "s"(kb), "n"(VM), "v"(vo), "s"(vb) : "memory", "scc");
+}
+// f(integral_constant<int, I>) for I = 0 .. N-1, each I a compile-time constant
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 __device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t m0v) {
   uint32_t save;
@@ -166,7 +180,7 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
 
   // ---- DMA: per-lane byte offsets relative to the tile's first key (constant across tiles) ----
   const int64_t key_stride = (int64_t)hkv * D * 2;   // bytes between consecutive keys
-  uint32_t koff[C::LPW], voff[C::LPW], ldsk[C::LPW];
+  uint32_t koff[C::LPW], voff[C::LPW];
   int lrow[C::LPW];
 #pragma unroll
   for (int i = 0; i < C::LPW; ++i) {
@@ -174,27 +188,27 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
     lrow[i] = r;
     koff[i] = (uint32_t)(r * key_stride) + 16 * ((lane % C::CPR) ^ S::k(r));
     voff[i] = (uint32_t)(r * key_stride) + 16 * ((lane % C::CPR) ^ S::v(r));
-    ldsk[i] = (uint32_t)((wave * C::LPW + i) * 1024);
   }
   const char* kbase = reinterpret_cast<const char*>(k) + (int64_t)kvh * D * 2;
   const char* vbase = reinterpret_cast<const char*>(v) + (int64_t)kvh * D * 2;
-  auto issue_tile = [&](int t, int buf) {
+  const uint32_t ldsw = lds0 + (uint32_t)(wave * C::LPW * 1024);   // this wave's pieces of a tile
+  auto issue_tile = [&](int t, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int kb = t * kBN;
     const char* kt_g = kbase + kb * key_stride;
     const char* vt_g = vbase + kb * key_stride;
     if (kb + kBN <= m) {
-#pragma unroll
-      for (int i = 0; i < C::LPW; ++i) {
-        dma16x2(koff[i], kt_g, lds0 + C::K0 + buf * C::TILE + ldsk[i], voff[i], vt_g,
-                lds0 + C::V0 + buf * C::TILE + ldsk[i]);
-      }
+      static_for<C::LPW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        dma16x2<C::K0 + buf * C::TILE + 1024 * i, C::V0 + buf * C::TILE + 1024 * i>(ldsw, koff[i], kt_g, voff[i], vt_g);
+      });
     } else {   // ragged last tile: keys past the end are clamped to the last key
-#pragma unroll
-      for (int i = 0; i < C::LPW; ++i) {
+      static_for<C::LPW>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
         const int64_t shift = (int64_t)(min(kb + lrow[i], m - 1) - (kb + lrow[i])) * key_stride;
-        dma16x2((uint32_t)(koff[i] + shift), kt_g, lds0 + C::K0 + buf * C::TILE + ldsk[i], (uint32_t)(voff[i] + shift),
-                vt_g, lds0 + C::V0 + buf * C::TILE + ldsk[i]);
-      }
+        dma16x2<C::K0 + buf * C::TILE + 1024 * i, C::V0 + buf * C::TILE + 1024 * i>(
+            ldsw, (uint32_t)(koff[i] + shift), kt_g, (uint32_t)(voff[i] + shift), vt_g);
+      });
     }
     const uint32_t soff = 4u * (uint32_t)(min(kb + lane, m - 1) - kb);
     if (BIAS && wave == 0) dma4(soff, s_kept + kb, lds0 + C::SB + buf * kBN * 4);
@@ -204,7 +218,7 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
     }
   };
   // the first K/V tile is in flight while Q is loaded and scaled
-  if (t_begin + grp < t_end) issue_tile(t_begin + grp, 0);
+  if (t_begin + grp < t_end) issue_tile(t_begin + grp, std::integral_constant<int, 0>{});
 
   bf16x8 qf[D / 16];
 #pragma unroll
@@ -391,7 +405,7 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
       for (int s = 0; s < KPRE; ++s)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) kp[s][kt] = read_k(s, kt, std::integral_constant<int, 0>{});
-      if (tt(j + 1) < t_end) issue_tile(tt(j + 1), 1);
+      if (tt(j + 1) < t_end) issue_tile(tt(j + 1), std::integral_constant<int, 1>{});
       if (KS == 1 || tt(j) < t_end) tile(tt(j), std::integral_constant<int, 0>{}, kp);
     }
     wait_dma();
@@ -402,7 +416,7 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
       for (int s = 0; s < KPRE; ++s)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) kp[s][kt] = read_k(s, kt, std::integral_constant<int, 1>{});
-      if (tt(j + 2) < t_end) issue_tile(tt(j + 2), 0);
+      if (tt(j + 2) < t_end) issue_tile(tt(j + 2), std::integral_constant<int, 0>{});
       if (KS == 1 || tt(j + 1) < t_end) tile(tt(j + 1), std::integral_constant<int, 1>{}, kp);
       wait_dma();
       __syncthreads();
