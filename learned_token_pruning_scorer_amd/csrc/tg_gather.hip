@@ -4,37 +4,41 @@
 // section "Jak to dziala").
 //
 // x_kept[r, :] = x[kept[r], :] and s_kept[r] = scores[kept[r]].  Pure data movement:
-// each workgroup copies kRows rows with 16-byte vector loads issued together before
-// the stores, so one 4 KiB row (d_model 2048, bf16) is one load per thread.
+// each workgroup copies ROWS rows with 16-byte vector loads issued together before
+// the stores, so one 4 KiB row (d_model 2048, bf16) is one load per thread.  8 rows per
+// workgroup from 8192 rows on (half the workgroups, twice the bytes in flight per thread;
+// at M = 8256 the 4-row grid, 2064 workgroups of 256 threads, is 16 more than the chip
+// holds at once), 4 below, where more workgroups spread the rows over more CUs.
 #include "tg_common.h"
 
 namespace tg {
 
 constexpr int kGatherThreads = 256;
-constexpr int kGatherRows = 4;
+constexpr int kGatherManyRows = 8192;   // from here on, 8 rows per workgroup
 
+template <int ROWS>
 __global__ __launch_bounds__(kGatherThreads) void gather_vec16_kernel(
     const char* __restrict__ x, int64_t ldx_bytes, int n, const int32_t* __restrict__ kept, int m,
     char* __restrict__ out, int64_t ldo_bytes, int pieces, const float* __restrict__ scores,
     float* __restrict__ s_kept) {
-  const int r0 = blockIdx.x * kGatherRows;
-  int src[kGatherRows];
-  bool live[kGatherRows];
+  const int r0 = blockIdx.x * ROWS;
+  int src[ROWS];
+  bool live[ROWS];
 #pragma unroll
-  for (int r = 0; r < kGatherRows; ++r) {
+  for (int r = 0; r < ROWS; ++r) {
     src[r] = (r0 + r < m) ? kept[r0 + r] : 0;
     live[r] = r0 + r < m && src[r] >= 0 && src[r] < n;   // out-of-range indices are skipped
   }
   for (int p = threadIdx.x; p < pieces; p += kGatherThreads) {
-    u32x4 v[kGatherRows];
+    u32x4 v[ROWS];
 #pragma unroll
-    for (int r = 0; r < kGatherRows; ++r)
+    for (int r = 0; r < ROWS; ++r)
       if (live[r]) v[r] = *reinterpret_cast<const u32x4*>(x + (int64_t)src[r] * ldx_bytes + 16 * (int64_t)p);
 #pragma unroll
-    for (int r = 0; r < kGatherRows; ++r)
+    for (int r = 0; r < ROWS; ++r)
       if (live[r]) *reinterpret_cast<u32x4*>(out + (int64_t)(r0 + r) * ldo_bytes + 16 * (int64_t)p) = v[r];
   }
-  if (scores && threadIdx.x < kGatherRows && live[threadIdx.x])
+  if (scores && threadIdx.x < ROWS && live[threadIdx.x])
     s_kept[r0 + threadIdx.x] = scores[src[threadIdx.x]];
 }
 
@@ -71,10 +75,12 @@ extern "C" tg_status tg_gather_kept(int32_t dtype, int64_t n, int32_t d_model, c
                           static_cast<uintptr_t>(row_bytes);
   const int mm = static_cast<int>(m);
   if ((align & 15u) == 0) {
-    const int grid = (mm + kGatherRows - 1) / kGatherRows;
-    hipLaunchKernelGGL(gather_vec16_kernel, dim3(grid), dim3(kGatherThreads), 0, st,
-                       static_cast<const char*>(x), ldx * esz, static_cast<int>(n), kept_idx, mm, static_cast<char*>(x_kept),
-                       ld_out * esz, static_cast<int>(row_bytes / 16), scores, s_kept);
+    const bool many = mm >= kGatherManyRows;
+    const int rows = many ? 8 : 4;
+    const int grid = (mm + rows - 1) / rows;
+    hipLaunchKernelGGL(many ? gather_vec16_kernel<8> : gather_vec16_kernel<4>, dim3(grid), dim3(kGatherThreads), 0,
+                       st, static_cast<const char*>(x), ldx * esz, static_cast<int>(n), kept_idx, mm,
+                       static_cast<char*>(x_kept), ld_out * esz, static_cast<int>(row_bytes / 16), scores, s_kept);
   } else if (esz == 2) {
     hipLaunchKernelGGL(gather_elem_kernel<uint16_t>, dim3(mm), dim3(kGatherThreads), 0, st,
                        static_cast<const uint16_t*>(x), ldx, static_cast<int>(n), kept_idx, mm, static_cast<uint16_t*>(x_kept),

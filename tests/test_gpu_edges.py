@@ -116,7 +116,11 @@ def test_score_f32_shapes(n, d_model, d_hidden):
 
 # --------------------------------------------------------------------------- gather
 @pytest.mark.parametrize("dtype,d_model,m", [("bf16", 2048, 1), ("bf16", 2048, 1001), ("bf16", 10, 33),
-                                             ("f32", 256, 77), ("f32", 5, 9)])
+                                             ("f32", 256, 77), ("f32", 5, 9),
+                                             # 8 rows per workgroup from 8192 rows: exact, ragged tails,
+                                             # rows narrower than the workgroup
+                                             ("bf16", 2048, 8192), ("bf16", 2048, 8197), ("f32", 256, 8195),
+                                             ("bf16", 64, 9003)])
 def test_gather_shapes(dtype, d_model, m):
     binding = require_gpu()
     import torch
