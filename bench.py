@@ -481,14 +481,15 @@ def main():
     also = None
     if args.also and args.also != args.workload:
         p2 = Path(args.also, binding, torch)
-        _, st2, _ = p2.timed(args.steps, args.warmup)
+        _, st2, st2m = p2.timed(args.steps, args.warmup)
         sec2e = p2.eager_period
         sec2 = p2.timed_graph(args.steps, args.warmup)
         sec2c = p2.timed_cold(max(5, args.steps // 2))
         also = {"workload": args.also, "tokens_per_s": p2.w.n / sec2, "ms_per_step": sec2 * 1e3,
                 "cold_ms_per_step": sec2c * 1e3, "cold_tokens_per_s": p2.w.n / sec2c,
                 "eager_ms_per_step": sec2e * 1e3, "eager_tokens_per_s": p2.w.n / sec2e,
-                "stage_us_mean": {"score": st2[0], "select": st2[1], "gather": st2[2], "attention": st2[3]}}
+                "stage_us_mean": {"score": st2[0], "select": st2[1], "gather": st2[2], "attention": st2[3]},
+                "stage_us_median": {"score": st2m[0], "select": st2m[1], "gather": st2m[2], "attention": st2m[3]}}
         del p2
         torch.cuda.empty_cache()
 
