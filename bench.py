@@ -34,7 +34,7 @@ CALIB_BYTES = 1 << 30          # streaming copy in --profile-steps mode: reads a
 # HBM bytes per launch of the attention kernel on long128k, from rocprofv3 FETCH_SIZE and WRITE_SIZE
 # scaled by the same counters' reading of the calibration copy (profiles/long128k_hbm_counters.md).
 # Reported only while the kernel source is the one the counters were taken on.
-ATTN_TRAFFIC = {"workload": "long128k", "bytes": 116942549,
+ATTN_TRAFFIC = {"workload": "long128k", "bytes": 116886749,
                 "source": "learned_token_pruning_scorer_amd/csrc/tg_attention.hip",
                 "sha256": "a9bb7310298659b24399b6e8412d8d04abf8245b1739c76501eafe27c9c514e9"}
 
