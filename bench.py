@@ -438,8 +438,8 @@ def cpu_baseline(name, score_rows, attn_rows):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the multi-GPU design is documented, not built)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the path is "
+              "implemented for one GPU, and how it would shard over several is a design only", file=sys.stderr)
         return 2
     import torch
     from learned_token_pruning_scorer_amd import binding
