@@ -30,6 +30,7 @@ def test_multi_budget_sweep_64k():
     (3001, 500, 2500, [0, 1, 777, 1999, 2000, 5000, 3, 1000]),   # eight budgets, mixed modes
     (70000, 0, 69936, [1, 64, 4096, 30000]),                        # chunks larger than the register keys
     (5000, 2500, 2500, [7, 9]),                                     # empty document
+    (140001, 1000, 139001, [0, 1, 4096, 8192, 65536, 138000, 200000, 17]),   # beyond the register keys
 ])
 def test_multi_budget_edges(n, db, de, ks):
     binding = require_gpu()
@@ -47,6 +48,7 @@ def test_multi_budget_edges(n, db, de, ks):
 @pytest.mark.parametrize("n,db,de,k,seed", [
     (1000, 0, 936, 100, 1), (1000, 0, 936, 100, 2), (131072, 0, 131008, 8192, 12345),
     (3001, 500, 2500, 0, 5), (3001, 500, 2500, 5000, 5), (70000, 64, 69000, 12345, 2**63 + 11),
+    (140001, 7, 139999, 70000, 99),
 ])
 def test_random_selector_matches_oracle(n, db, de, k, seed):
     binding = require_gpu()
