@@ -33,7 +33,7 @@ from scipy.special import erf as _erf
 __all__ = [
     "gelu", "gate_score", "num_kept", "select_topk", "select_topk_multi", "splitmix64", "random_keys",
     "select_random", "gather_kept", "gated_attention", "causal_attention", "gated_attention_lse",
-    "gated_attention_backward", "rope_inv_freq", "rope", "qkv_rope", "emit_kv",
+    "gated_attention_backward", "gated_attention_backward_rows", "rope_inv_freq", "rope", "qkv_rope", "emit_kv",
 ]
 
 
@@ -243,19 +243,21 @@ def causal_attention(q, k, v, rows=None):
 #     dgain[h]   = sum_j s_kept[j] sum_i dZ_h[i, j]
 #     dtau       = -(1 / tau) sum_{h,i,j} dZ_h[i, j] q_i . k_j / (sqrt(d) tau)
 # ----------------------------------------------------------------------------------------
-def gated_attention_lse(q, k, v, pos, s_kept, gain, tau):
-    """Natural-log log-sum-exp of each row's visible logits: float64 [M, Hq]."""
+def gated_attention_lse(q, k, v, pos, s_kept, gain, tau, rows=None):
+    """Natural-log log-sum-exp of each row's visible logits: float64 [len(rows), Hq]
+    (all M rows when rows is None)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     pos = np.asarray(pos, dtype=np.int64)
     m, hq, d = q.shape
+    rows = np.arange(m, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     group = hq // k.shape[1]
     use_bias = s_kept is not None and gain is not None
     scale = 1.0 / (math.sqrt(d) * float(tau))
-    visible = pos[None, :] <= pos[:, None]
-    lse = np.empty((m, hq))
+    visible = pos[None, :] <= pos[rows][:, None]
+    lse = np.empty((len(rows), hq))
     for h in range(hq):
-        logits = (q[:, h, :] @ k[:, h // group, :].T) * scale
+        logits = (q[rows, h, :] @ k[:, h // group, :].T) * scale
         if use_bias:
             logits = logits + float(gain[h]) * np.asarray(s_kept, dtype=np.float64)[None, :]
         logits = np.where(visible, logits, -np.inf)
@@ -320,6 +322,71 @@ def gated_attention_backward(q, k, v, pos, s_kept, gain, tau, dout, magnitudes=F
     if magnitudes:
         return dq, dk, dv, ds, dgain, dtau, {"dgain": mag_gain, "dtau": mag_tau}
     return dq, dk, dv, ds, dgain, dtau
+
+
+def gated_attention_backward_rows(q, k, v, pos, s_kept, gain, tau, dout, out, lse, q_rows, k_rows):
+    """Selected rows of the same gradient, float64: dq at the query rows q_rows, and dk, dv
+    and ds_kept at the key rows k_rows (ds_kept None when the bias is off), given the
+    forward's output `out` [M, Hq, d] and natural-log log-sum-exp `lse` [M, Hq].
+
+    With those two, every term is local to one row or one key: the softmax weight of key j
+    for query i is P_ij = exp(z_ij - lse_i) (z the gated logit, -inf where pos_j > pos_i),
+    the row's correction is D_i = dout_i . out_i (= sum_j P_ij dout_i . v_j), and the logit
+    gradient is dZ_ij = P_ij (dout_i . v_j - D_i).  Then dq_i = scale sum_j dZ_ij k_j,
+    dk_j = scale sum_i dZ_ij q_i and dv_j = sum_i P_ij dout_i (summed over the query heads
+    of the key's group), ds_j = sum_h gain_h sum_i dZ_ij.  A row costs O(M d) per head,
+    so sampled rows of a large problem are cheap where the whole gradient is not."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    out = np.asarray(out, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    pos = np.asarray(pos, dtype=np.int64)
+    q_rows = np.asarray(q_rows, dtype=np.int64)
+    k_rows = np.asarray(k_rows, dtype=np.int64)
+    m, hq, d = q.shape
+    hkv = k.shape[1]
+    group = hq // hkv
+    use_bias = s_kept is not None and gain is not None
+    if use_bias:
+        s_kept = np.asarray(s_kept, dtype=np.float64)
+        gain = np.asarray(gain, dtype=np.float64)
+    scale = 1.0 / (math.sqrt(d) * float(tau))
+    dsum = np.sum(dout * out, axis=2)                          # D_i per head: [M, Hq]
+    # per-head [M, d] slices, contiguous (each is read once per selected row)
+    qh = [np.ascontiguousarray(q[:, h, :]) for h in range(hq)]
+    doh = [np.ascontiguousarray(dout[:, h, :]) for h in range(hq)]
+    kg = [np.ascontiguousarray(k[:, g, :]) for g in range(hkv)]
+    vg = [np.ascontiguousarray(v[:, g, :]) for g in range(hkv)]
+    dq = np.zeros((len(q_rows), hq, d))
+    for a, i in enumerate(q_rows):
+        visible = pos <= pos[i]
+        for h in range(hq):
+            g = h // group
+            z = (kg[g] @ q[i, h, :]) * scale
+            if use_bias:
+                z = z + gain[h] * s_kept
+            p = np.where(visible, np.exp(np.where(visible, z, 0.0) - lse[i, h]), 0.0)
+            dz = p * (vg[g] @ dout[i, h, :] - dsum[i, h])
+            dq[a, h, :] = scale * (dz @ kg[g])
+    dk = np.zeros((len(k_rows), hkv, d))
+    dv = np.zeros((len(k_rows), hkv, d))
+    ds = np.zeros(len(k_rows)) if use_bias else None
+    for b, j in enumerate(k_rows):
+        visible = pos[j] <= pos                                 # query rows that see key j
+        for h in range(hq):
+            g = h // group
+            z = (qh[h] @ k[j, g, :]) * scale
+            if use_bias:
+                z = z + gain[h] * s_kept[j]
+            p = np.where(visible, np.exp(np.where(visible, z, 0.0) - lse[:, h]), 0.0)
+            dz = p * (doh[h] @ v[j, g, :] - dsum[:, h])
+            dk[b, g, :] += scale * (dz @ qh[h])
+            dv[b, g, :] += p @ doh[h]
+            if use_bias:
+                ds[b] += gain[h] * dz.sum()
+    return dq, dk, dv, ds
 
 
 # ----------------------------------------------------------------------------------------

@@ -104,6 +104,38 @@ def test_backward_matches_oracle(case):
     assert lerr.max() <= 2e-2
 
 
+def test_backward_at_the_128k_workload_size_on_sampled_rows():
+    """M = 8256 (the 128k workload's kept rows), Hq 16, Hkv 8, d 128, bias on, gapped positions,
+    in the launch configuration the benchmark times.  The whole gradient is out of the
+    oracle's reach at this size, so: the GPU's output and log-sum-exp on 64 sampled query rows
+    against the oracle's, then dq on those rows and dk, dv, ds_kept on 64 sampled key rows
+    against the oracle's per-row gradient fed the GPU's output and log-sum-exp (each stage
+    checked on its own upstream, as for the forward)."""
+    binding = require_gpu()
+    m, hq, hkv, d = 8256, 16, 8, 128
+    tau = 1.1
+    q, k, v, dout, pos, s, gain = _case_inputs(m, hq, hkv, d, True, seed=128)
+    log(f"[attention backward, sampled rows] m={m} hq={hq} hkv={hkv} d={d}")
+    out, lse, (dq, dk, dv, ds, _, _) = _run(binding, q, k, v, dout, pos, s, gain, tau, True)
+    qr = inputs.sample_rows(m, 64, forced=(0, m - 1), seed=3)
+    kr = inputs.sample_rows(m, 64, forced=(0, m - 1), seed=4)
+    f64 = lambda a: inputs.to_f64(a, "bf16")
+    Q, K, V, dO = f64(q), f64(k), f64(v), f64(dout)
+    o_gpu, l_gpu = host_f64(out), host_f64(lse)
+    ro = oracle.gated_attention(Q, K, V, pos, s, gain, tau, rows=qr)
+    eo = np.abs(o_gpu[qr] - ro)
+    log(f"  out: max_abs={eo.max():.3e} mean_abs={eo.mean():.3e}")
+    assert eo.max() <= 2e-2 and eo.mean() <= 2e-3
+    el = np.abs(l_gpu[qr] - oracle.gated_attention_lse(Q, K, V, pos, s, gain, tau, rows=qr))
+    log(f"  lse: max_abs={el.max():.3e}")
+    assert el.max() <= 2e-2
+    rq, rk, rv, rs = oracle.gated_attention_backward_rows(Q, K, V, pos, s, gain, tau, dO, o_gpu, l_gpu, qr, kr)
+    _check_tensor("dq", host_f64(dq)[qr], rq)
+    _check_tensor("dk", host_f64(dk)[kr], rk)
+    _check_tensor("dv", host_f64(dv)[kr], rv)
+    _check_tensor("ds_kept", host_f64(ds)[kr], rs)
+
+
 def test_lse_variant_leaves_the_output_unchanged():
     """tg_gated_attention_lse writes the same output bits as tg_gated_attention."""
     binding = require_gpu()

@@ -537,3 +537,30 @@ def test_emit_kv_writes_only_its_slots():
     np.testing.assert_array_equal(kc2[slot0:slot0 + m], k)
     np.testing.assert_array_equal(vc2[slot0:slot0 + m], v)
     np.testing.assert_array_equal(pc2[slot0:slot0 + m], pos)
+
+
+@pytest.mark.parametrize("bias", [True, False])
+def test_backward_rows_equal_the_whole_gradient(bias):
+    """The per-row form (P from the forward's lse, D_i = dout_i . out_i) gives the same rows as
+    the whole-matrix gradient, which autograd and finite differences pin above."""
+    g = np.random.default_rng(21 + bias)
+    m, hq, hkv, d = 70, 4, 2, 16
+    q, k, v, dout = (g.normal(size=(m, h, d)) for h in (hq, hkv, hkv, hq))
+    pos = np.sort(g.choice(300, m, replace=False))
+    s = g.normal(size=m) * 2 if bias else None
+    gain = g.uniform(0.5, 1.5, size=hq) if bias else None
+    tau = 0.9
+    out = oracle.gated_attention(q, k, v, pos, s, gain, tau)
+    lse = oracle.gated_attention_lse(q, k, v, pos, s, gain, tau)
+    dq, dk, dv, ds, _, _ = oracle.gated_attention_backward(q, k, v, pos, s, gain, tau, dout)
+    qr, kr = np.array([0, 5, 33, m - 1]), np.array([0, 17, 40, m - 1])
+    rq, rk, rv, rs = oracle.gated_attention_backward_rows(q, k, v, pos, s, gain, tau, dout, out, lse, qr, kr)
+    assert np.allclose(rq, dq[qr], rtol=1e-10, atol=1e-12)
+    assert np.allclose(rk, dk[kr], rtol=1e-10, atol=1e-12)
+    assert np.allclose(rv, dv[kr], rtol=1e-10, atol=1e-12)
+    if bias:
+        assert np.allclose(rs, ds[kr], rtol=1e-10, atol=1e-12)
+    else:
+        assert rs is None
+    # the row subset of the log-sum-exp is the same rows of the whole one
+    assert np.allclose(oracle.gated_attention_lse(q, k, v, pos, s, gain, tau, rows=qr), lse[qr], rtol=0, atol=1e-13)
