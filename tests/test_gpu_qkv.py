@@ -76,6 +76,33 @@ def test_qkv_rope_matches_oracle(case):
         assert np.all(bits == SENTINEL)
 
 
+def test_qkv_rope_at_the_128k_workload_size_on_sampled_rows():
+    """M = 8256 kept rows of d_model 2048 to Hq 16 / Hkv 8 heads of 128, positions from a
+    131072-token prompt, in the launch configuration the benchmark times; the projection is
+    row-local, so the oracle computes 64 sampled rows (the first and last forced) on their own."""
+    binding = require_gpu()
+    import torch
+    g = np.random.default_rng(8256)
+    m, d_model, hq, hkv, d = 8256, 2048, 16, 8, 128
+    n_feat = (hq + 2 * hkv) * d
+    x = inputs.f32_to_bf16_bits(g.normal(size=(m, d_model)).astype(np.float32))
+    w = inputs.f32_to_bf16_bits((g.normal(size=(n_feat, d_model)) / np.sqrt(d_model)).astype(np.float32))
+    pos = np.sort(g.choice(131072, m, replace=False)).astype(np.int32)
+    theta = 1e6
+    log(f"[qkv_rope, sampled rows] m={m} d_model={d_model} hq={hq} hkv={hkv} d={d}")
+    pc = torch.full((m,), -7, dtype=torch.int32, device="cuda")
+    q, kc, vc, pc = binding.tg_qkv_rope(binding.to_device(x, "bf16"), binding.to_device(w, "bf16"),
+                                        torch.from_numpy(pos).cuda(), hq, hkv, d, theta, pos_cache=pc)
+    torch.cuda.synchronize()
+    rows = inputs.sample_rows(m, 64, forced=(0, m - 1), seed=5)
+    rq, rk, rv = oracle.qkv_rope(inputs.to_f64(x[rows], "bf16"), inputs.to_f64(w, "bf16"), None, hq, hkv, d,
+                                 pos[rows], theta)
+    _check("q", host_f64(q)[rows], rq)
+    _check("k", host_f64(kc)[rows], rk)
+    _check("v", host_f64(vc)[rows], rv)
+    np.testing.assert_array_equal(pc.cpu().numpy(), pos)
+
+
 def test_qkv_rope_without_position_cache_and_large_positions():
     """Positions near 2^31 (angles of ~2e9 rad) still rotate accurately."""
     binding = require_gpu()
