@@ -270,11 +270,23 @@ def gated_attention_backward(q, k, v, pos, s_kept, gain, tau, dout, magnitudes=F
     """Gradients (dq, dk, dv, ds_kept, dgain, dtau) of sum(out * dout), float64.
     ds_kept and dgain are None when the bias is off.
 
-    With magnitudes=True a seventh item is returned: {"dgain": [Hq], "dtau": float},
-    the same sums taken over absolute values of their terms (sum_j |s_j col_j| per
-    head, and sum |dZ q.k| scale / tau).  dgain and dtau are sums with heavy
-    cancellation (each row of dZ sums to zero), so these are the scales against
-    which a rounding error in them is judged."""
+    With magnitudes=True a seventh item is returned: a dict holding, for every output,
+    the same expression with every sum taken over the absolute values of its terms --
+    the scale against which a rounding error in that output is judged (the outputs are
+    sums whose terms cancel: each row of dZ sums to zero, and dZ itself is a difference):
+        |dP|_ij   = |dout_i| . |v_j|,   |D|_i = |dout_i| . |out_i|   (D_i = dout_i . out_i)
+        |dZ|_ij   = P_ij (|dP|_ij + |D|_i)
+        "dq"      [M, Hq, d]  scale sum_j |dZ|_ij |k_j|
+        "dk"      [M, Hkv, d] scale sum_{h in g} sum_i |dZ|_ij |q_i|
+        "dv"      [M, Hkv, d] sum_{h in g} sum_i P_ij |dout_i|
+        "ds_kept" [M]         sum_h |gain_h| sum_i |dZ|_ij          (None when the bias is off)
+        "dgain"   [Hq]        sum_j |s_j| |sum_i dZ_ij|
+        "dtau"    float       sum |dZ_ij q_i.k_j| scale / tau
+    and, for dq, dk, dv and ds_kept, the root-sum-square of the same terms ("dq_rss", ...),
+    the size that independent rounding errors of the terms add up to, with the term of dZ
+    taken as a_ij = P_ij (|dout_i . v_j| + |D_i|):
+        "dq_rss" = scale sqrt(sum_j a_ij^2 k_j^2)        "dk_rss" = scale sqrt(sum_{h,i} a_ij^2 q_i^2)
+        "dv_rss" = sqrt(sum_{h,i} P_ij^2 dout_i^2)       "ds_kept_rss" = sqrt(sum_h gain_h^2 sum_i a_ij^2)"""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -295,6 +307,11 @@ def gated_attention_backward(q, k, v, pos, s_kept, gain, tau, dout, magnitudes=F
     dtau = 0.0
     mag_gain = np.zeros(hq)
     mag_tau = 0.0
+    if magnitudes:
+        mag_dq, mag_dk, mag_dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+        mag_ds = np.zeros(m) if use_bias else None
+        sq_dq, sq_dk, sq_dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)   # sums of squares
+        sq_ds = np.zeros(m) if use_bias else None
     for h in range(hq):
         g = h // group
         qk = q[:, h, :] @ k[:, g, :].T
@@ -319,12 +336,31 @@ def gated_attention_backward(q, k, v, pos, s_kept, gain, tau, dout, magnitudes=F
             mag_gain[h] = float(np.dot(np.abs(col), np.abs(s_kept)))
         dtau += -float(np.sum(dz * qk)) * scale / float(tau)
         mag_tau += float(np.sum(np.abs(dz * qk))) * scale / float(tau)
+        if magnitudes:
+            adz = p * (np.abs(dout[:, h, :]) @ np.abs(v[:, g, :]).T
+                       + np.sum(np.abs(dout[:, h, :] * o), axis=1, keepdims=True))
+            mag_dq[:, h, :] = (adz @ np.abs(k[:, g, :])) * scale
+            mag_dk[:, g, :] += (adz.T @ np.abs(q[:, h, :])) * scale
+            mag_dv[:, g, :] += p.T @ np.abs(dout[:, h, :])
+            if use_bias:
+                mag_ds += abs(gain[h]) * adz.sum(axis=0)
+            a2 = (p * (np.abs(dp) + np.abs(dsum))) ** 2
+            sq_dq[:, h, :] = (a2 @ k[:, g, :] ** 2) * scale ** 2
+            sq_dk[:, g, :] += (a2.T @ q[:, h, :] ** 2) * scale ** 2
+            sq_dv[:, g, :] += (p ** 2).T @ dout[:, h, :] ** 2
+            if use_bias:
+                sq_ds += gain[h] ** 2 * a2.sum(axis=0)
     if magnitudes:
-        return dq, dk, dv, ds, dgain, dtau, {"dgain": mag_gain, "dtau": mag_tau}
+        return dq, dk, dv, ds, dgain, dtau, {"dq": mag_dq, "dk": mag_dk, "dv": mag_dv, "ds_kept": mag_ds,
+                                             "dgain": mag_gain, "dtau": mag_tau,
+                                             "dq_rss": np.sqrt(sq_dq), "dk_rss": np.sqrt(sq_dk),
+                                             "dv_rss": np.sqrt(sq_dv),
+                                             "ds_kept_rss": np.sqrt(sq_ds) if use_bias else None}
     return dq, dk, dv, ds, dgain, dtau
 
 
-def gated_attention_backward_rows(q, k, v, pos, s_kept, gain, tau, dout, out, lse, q_rows, k_rows):
+def gated_attention_backward_rows(q, k, v, pos, s_kept, gain, tau, dout, out, lse, q_rows, k_rows,
+                                  magnitudes=False):
     """Selected rows of the same gradient, float64: dq at the query rows q_rows, and dk, dv
     and ds_kept at the key rows k_rows (ds_kept None when the bias is off), given the
     forward's output `out` [M, Hq, d] and natural-log log-sum-exp `lse` [M, Hq].
@@ -335,7 +371,11 @@ def gated_attention_backward_rows(q, k, v, pos, s_kept, gain, tau, dout, out, ls
     gradient is dZ_ij = P_ij (dout_i . v_j - D_i).  Then dq_i = scale sum_j dZ_ij k_j,
     dk_j = scale sum_i dZ_ij q_i and dv_j = sum_i P_ij dout_i (summed over the query heads
     of the key's group), ds_j = sum_h gain_h sum_i dZ_ij.  A row costs O(M d) per head,
-    so sampled rows of a large problem are cheap where the whole gradient is not."""
+    so sampled rows of a large problem are cheap where the whole gradient is not.
+
+    With magnitudes=True a fifth item is returned: the per-element sums of absolute terms
+    and root-sum-squares of the terms of dq, dk, dv and ds_kept at those rows, as
+    gated_attention_backward defines them."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -354,12 +394,14 @@ def gated_attention_backward_rows(q, k, v, pos, s_kept, gain, tau, dout, out, ls
         gain = np.asarray(gain, dtype=np.float64)
     scale = 1.0 / (math.sqrt(d) * float(tau))
     dsum = np.sum(dout * out, axis=2)                          # D_i per head: [M, Hq]
+    dsum_abs = np.sum(np.abs(dout * out), axis=2)              # its terms' magnitudes
     # per-head [M, d] slices, contiguous (each is read once per selected row)
     qh = [np.ascontiguousarray(q[:, h, :]) for h in range(hq)]
     doh = [np.ascontiguousarray(dout[:, h, :]) for h in range(hq)]
     kg = [np.ascontiguousarray(k[:, g, :]) for g in range(hkv)]
     vg = [np.ascontiguousarray(v[:, g, :]) for g in range(hkv)]
     dq = np.zeros((len(q_rows), hq, d))
+    mq, sqq = np.zeros_like(dq), np.zeros_like(dq)
     for a, i in enumerate(q_rows):
         visible = pos <= pos[i]
         for h in range(hq):
@@ -368,11 +410,20 @@ def gated_attention_backward_rows(q, k, v, pos, s_kept, gain, tau, dout, out, ls
             if use_bias:
                 z = z + gain[h] * s_kept
             p = np.where(visible, np.exp(np.where(visible, z, 0.0) - lse[i, h]), 0.0)
-            dz = p * (vg[g] @ dout[i, h, :] - dsum[i, h])
+            dp = vg[g] @ dout[i, h, :]
+            dz = p * (dp - dsum[i, h])
             dq[a, h, :] = scale * (dz @ kg[g])
+            if magnitudes:
+                adz = p * (np.abs(vg[g]) @ np.abs(dout[i, h, :]) + dsum_abs[i, h])
+                mq[a, h, :] = scale * (adz @ np.abs(kg[g]))
+                sqq[a, h, :] = scale ** 2 * ((p * (np.abs(dp) + abs(dsum[i, h]))) ** 2 @ kg[g] ** 2)
     dk = np.zeros((len(k_rows), hkv, d))
     dv = np.zeros((len(k_rows), hkv, d))
     ds = np.zeros(len(k_rows)) if use_bias else None
+    mk, mv = np.zeros_like(dk), np.zeros_like(dv)
+    ms = np.zeros(len(k_rows)) if use_bias else None
+    sqk, sqv = np.zeros_like(dk), np.zeros_like(dv)
+    sqs = np.zeros(len(k_rows)) if use_bias else None
     for b, j in enumerate(k_rows):
         visible = pos[j] <= pos                                 # query rows that see key j
         for h in range(hq):
@@ -381,11 +432,27 @@ def gated_attention_backward_rows(q, k, v, pos, s_kept, gain, tau, dout, out, ls
             if use_bias:
                 z = z + gain[h] * s_kept[j]
             p = np.where(visible, np.exp(np.where(visible, z, 0.0) - lse[:, h]), 0.0)
-            dz = p * (doh[h] @ v[j, g, :] - dsum[:, h])
+            dp = doh[h] @ v[j, g, :]
+            dz = p * (dp - dsum[:, h])
             dk[b, g, :] += scale * (dz @ qh[h])
             dv[b, g, :] += p @ doh[h]
             if use_bias:
                 ds[b] += gain[h] * dz.sum()
+            if magnitudes:
+                adz = p * (np.abs(doh[h]) @ np.abs(v[j, g, :]) + dsum_abs[:, h])
+                mk[b, g, :] += scale * (adz @ np.abs(qh[h]))
+                mv[b, g, :] += p @ np.abs(doh[h])
+                if use_bias:
+                    ms[b] += abs(gain[h]) * adz.sum()
+                a2 = (p * (np.abs(dp) + np.abs(dsum[:, h]))) ** 2
+                sqk[b, g, :] += scale ** 2 * (a2 @ qh[h] ** 2)
+                sqv[b, g, :] += p ** 2 @ doh[h] ** 2
+                if use_bias:
+                    sqs[b] += gain[h] ** 2 * a2.sum()
+    if magnitudes:
+        return dq, dk, dv, ds, {"dq": mq, "dk": mk, "dv": mv, "ds_kept": ms, "dq_rss": np.sqrt(sqq),
+                                "dk_rss": np.sqrt(sqk), "dv_rss": np.sqrt(sqv),
+                                "ds_kept_rss": np.sqrt(sqs) if use_bias else None}
     return dq, dk, dv, ds
 
 

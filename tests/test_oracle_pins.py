@@ -564,3 +564,57 @@ def test_backward_rows_equal_the_whole_gradient(bias):
         assert rs is None
     # the row subset of the log-sum-exp is the same rows of the whole one
     assert np.allclose(oracle.gated_attention_lse(q, k, v, pos, s, gain, tau, rows=qr), lse[qr], rtol=0, atol=1e-13)
+
+
+def test_backward_magnitudes_bound_the_gradients():
+    """The per-element sums of absolute terms (the tolerance scale of the GPU gradient tests)
+    bound every gradient element; with dout >= 0 every term of dv is non-negative, so dv's
+    magnitude IS dv; flipping dout's sign flips the gradients and leaves the magnitudes; the
+    per-row form gives the same magnitudes as the whole-matrix form."""
+    g = np.random.default_rng(31)
+    m, hq, hkv, d = 60, 4, 2, 16
+    q, k, v, dout = (g.normal(size=(m, h, d)) for h in (hq, hkv, hkv, hq))
+    pos = np.sort(g.choice(200, m, replace=False))
+    s = g.normal(size=m) * 2
+    gain = g.uniform(0.5, 1.5, size=hq)
+    tau = 1.1
+    res = oracle.gated_attention_backward(q, k, v, pos, s, gain, tau, dout, magnitudes=True)
+    dq, dk, dv, ds, dgain, dtau, mag = res
+    for name, gr in (("dq", dq), ("dk", dk), ("dv", dv), ("ds_kept", ds)):
+        assert np.all(np.abs(gr) <= mag[name] * (1 + 1e-12) + 1e-15), name
+        assert np.all(mag[name] >= 0)
+    assert np.all(np.abs(dgain) <= mag["dgain"] * (1 + 1e-12))
+    assert abs(dtau) <= mag["dtau"] * (1 + 1e-12)
+    # dout >= 0: dv's terms P_ij dout_i are all non-negative
+    dpos = np.abs(dout)
+    _, _, dv2, _, _, _, mag2 = oracle.gated_attention_backward(q, k, v, pos, s, gain, tau, dpos, magnitudes=True)
+    np.testing.assert_allclose(mag2["dv"], dv2, rtol=1e-12, atol=1e-14)
+    # sign of dout
+    neg = oracle.gated_attention_backward(q, k, v, pos, s, gain, tau, -dout, magnitudes=True)
+    for a, b in zip(neg[:4], res[:4]):
+        np.testing.assert_allclose(a, -b, rtol=1e-12, atol=1e-14)
+    for name in ("dq", "dk", "dv", "ds_kept"):
+        np.testing.assert_allclose(neg[6][name], mag[name], rtol=1e-12, atol=1e-14)
+    # rows form
+    out = oracle.gated_attention(q, k, v, pos, s, gain, tau)
+    lse = oracle.gated_attention_lse(q, k, v, pos, s, gain, tau)
+    qr, kr = np.array([0, 9, 31, m - 1]), np.array([0, 12, 44, m - 1])
+    *_, rmag = oracle.gated_attention_backward_rows(q, k, v, pos, s, gain, tau, dout, out, lse, qr, kr,
+                                                    magnitudes=True)
+    np.testing.assert_allclose(rmag["dq"], mag["dq"][qr], rtol=1e-10)
+    np.testing.assert_allclose(rmag["dk"], mag["dk"][kr], rtol=1e-10)
+    np.testing.assert_allclose(rmag["dv"], mag["dv"][kr], rtol=1e-10)
+    np.testing.assert_allclose(rmag["ds_kept"], mag["ds_kept"][kr], rtol=1e-10)
+    for name in ("dq", "dk", "dv", "ds_kept"):
+        sub = qr if name == "dq" else kr
+        np.testing.assert_allclose(rmag[name + "_rss"], mag[name + "_rss"][sub], rtol=1e-10)
+    # root-sum-square <= sum of absolute values, element by element
+    for name in ("dq", "dk", "dv", "ds_kept"):
+        assert np.all(mag[name + "_rss"] <= mag[name] * (1 + 1e-12) + 1e-15), name
+    # a single query and key: P = 1 and every gradient element is one term per head, so
+    # dv's root-sum-square over the group's query heads is the norm of their dout values
+    one = oracle.gated_attention_backward(q[:1], k[:1], v[:1], pos[:1], s[:1], gain, tau, dout[:1],
+                                          magnitudes=True)[6]
+    grp = hq // hkv
+    np.testing.assert_allclose(one["dv_rss"][0], np.sqrt((dout[0] ** 2).reshape(hkv, grp, d).sum(axis=1)),
+                               rtol=1e-12)
