@@ -2,13 +2,15 @@
 """Throughput of the TokenGate gated-prefill hot path on one MI355X.
 
 One step = the whole path over one prompt already resident in HBM:
-    tg_gate_score (N rows) -> tg_select_topk -> tg_gather_kept -> tg_gated_attention_split (M rows)
+    tg_gate_score (N rows) -> tg_select_gather (top-K select + gather of the kept rows,
+    one launch) -> tg_gated_attention_split (M rows)
 (the gated attention with the library's own launch plan: at long contexts it is the plain
-tg_gated_attention kernel).  The four launches of a step are captured once in a HIP graph
+tg_gated_attention kernel).  The three launches of a step are captured once in a HIP graph
 (torch.cuda.CUDAGraph over the library's calls) and replayed: `value` = prompt tokens per
 second = N / (wall time of one step), K replays timed back-to-back between two device
-synchronisations.  Per-stage times come from HIP events recorded on the launch stream
-inside K eager steps of the same path.
+synchronisations (warm caches: nothing is flushed between replays; `cold_ms_per_step` is
+the same step after a 1 GiB fill).  Per-stage times come from HIP events recorded on the
+launch stream inside K eager steps of the same path.
 
 Prints ONE JSON line.  Inputs are seeded synthetic tensors of the workload's
 shape (no dataset, no trained weights): see learned_token_pruning_scorer_amd/inputs.py.
@@ -21,7 +23,13 @@ import os
 import sys
 import time
 
-import numpy as np
+# The CPU baseline's BLAS threads: the host cores this process may use, fixed before NumPy
+# loads its BLAS (a value already in the environment, e.g. the GPU machine's own, is kept).
+_HOST_CORES = len(os.sched_getaffinity(0))
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(_HOST_CORES))
+
+import numpy as np   # noqa: E402
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
@@ -31,6 +39,7 @@ METRIC = "gated-prefill input tokens/s at 16k/128k; attn TFLOP/s and select GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 CALIB_BYTES = 1 << 30          # streaming copy in --profile-steps mode: reads and writes this many bytes
+STAGES = ("score", "select_gather", "attention")   # the step's launches, in order
 # HBM bytes per launch of the attention kernel on long128k, from rocprofv3 FETCH_SIZE and WRITE_SIZE
 # scaled by the same counters' reading of the calibration copy (profiles/long128k_hbm_counters.md).
 # Reported only while the kernel source is the one the counters were taken on.
@@ -45,7 +54,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="long128k")
-    ap.add_argument("--also", default="niah16k", help="second workload reported beside the main one ('' = none)")
+    ap.add_argument("--also", default="niah16k,mdqa32k",
+                    help="comma-separated workloads reported beside the main one ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-score-rows", type=int, default=131072)
     ap.add_argument("--cpu-attn-rows", type=int, default=0, help="query rows of the CPU attention sample (0 = all)")
@@ -69,7 +79,7 @@ def algorithmic(w, k):
     gather_bytes = 2 * m * w.d_model * esz + m * 4 + 2 * m * 4
     attn_flops = 4.0 * w.head_dim * w.n_q_heads * m * (m + 1) / 2
     return dict(m=m, score_bytes=score_bytes, score_flops=score_flops, select_bytes=select_bytes,
-                gather_bytes=gather_bytes, attn_flops=attn_flops)
+                gather_bytes=gather_bytes, select_gather_bytes=select_bytes + gather_bytes, attn_flops=attn_flops)
 
 
 class Path:
@@ -97,7 +107,7 @@ class Path:
         # Q/K/V of the kept rows (their projection from hidden states is not part of the path)
         binding.tg_gate_score(self.x, self.w1, self.w2, self.b1, gi.b2, out=self.scores)
         binding.tg_select_topk(self.scores, w.doc_begin, w.doc_end, self.k, out=self.kept, workspace=self.ws)
-        torch.cuda.synchronize()
+        binding.tg_select_check(self.ws)
         if full_qkv is not None:
             idx = self.kept.long()
             self.q, self.kk, self.v = (t.index_select(0, idx).contiguous() for t in full_qkv)
@@ -127,12 +137,11 @@ class Path:
         if ev: ev[0].record()
         b.tg_gate_score(self.x, self.w1, self.w2, self.b1, self.gi.b2, out=self.scores)
         if ev: ev[1].record()
-        b.tg_select_topk(self.scores, w.doc_begin, w.doc_end, self.k, out=self.kept, workspace=self.ws)
+        b.tg_select_gather(self.scores, self.x, w.doc_begin, w.doc_end, self.k, kept=self.kept, x_kept=self.xk,
+                           s_kept=self.sk, workspace=self.ws)
         if ev: ev[2].record()
-        b.tg_gather_kept(self.x, self.kept, self.scores, out=self.xk, s_out=self.sk)
-        if ev: ev[3].record()
         self.attention()
-        if ev: ev[4].record()
+        if ev: ev[3].record()
 
     def graph(self):
         """The step captured in a HIP graph (after warm-up launches on a side stream)."""
@@ -185,14 +194,15 @@ class Path:
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             self.step(evs[i])
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evs]) * 1e3   # us
+        self.b.tg_select_check(self.ws)
+        stage = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(len(STAGES))] for e in evs]) * 1e3   # us
         # step period on the GPU timeline (start of one step to the start of the next), median:
         # robust to a host hiccup, which the wall-clock mean is not
         period = [evs[i][0].elapsed_time(evs[i + 1][0]) for i in range(steps - 1)] or [wall * 1e3]
@@ -248,6 +258,18 @@ def next_rows(path, reps):
     us_fwd = _event_time_us(torch, lambda: b.tg_gated_attention_lse(
         path.q, path.kk, path.v, path.kept, path.sk, path.gain, path.tau, out=out, lse=lse), reps)
     res["attention_forward_with_lse"] = {"us": us_fwd}
+    # the same selection and gather as two launches (tg_select_topk, then tg_gather_kept)
+    kept2 = torch.empty_like(path.kept)
+    xk2, sk2 = torch.empty_like(path.xk), torch.empty_like(path.sk)
+
+    def two_calls():
+        b.tg_select_topk(path.scores, w.doc_begin, w.doc_end, path.k, out=kept2, workspace=path.ws)
+        b.tg_gather_kept(path.x, kept2, path.scores, out=xk2, s_out=sk2)
+    us = _event_time_us(torch, two_calls, reps)
+    byts = algorithmic(w, path.k)["select_gather_bytes"]
+    res["select_then_gather"] = {"us": us, "frac_hbm_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                 "note": "tg_select_topk then tg_gather_kept (two launches) on the step's inputs"}
+    del kept2, xk2, sk2
     # several budgets over one histogram of the same scores
     ks = [path.k // 8, path.k // 4, path.k // 2, path.k]
     outs = torch.empty(sum(w.n_kept(k) for k in ks), dtype=torch.int32, device="cuda")
@@ -334,7 +356,7 @@ def sweep64k(binding, torch, steps, warmup):
         sec = p.timed_graph(steps, warmup)
         out["points"].append({"k": k, "m": p.m, "ms_per_step": sec * 1e3, "eager_ms_per_step": sec_e * 1e3,
                               "peak_bytes": peak,
-                              "stage_us_mean": {"score": st[0], "select": st[1], "gather": st[2], "attention": st[3]}})
+                              "stage_us_mean": dict(zip(STAGES, (float(v) for v in st)))})
         del p
         torch.cuda.empty_cache()
     # peak device bytes of the unpruned layer: X, Q/K/V of all N rows, output, run once
@@ -427,6 +449,8 @@ def cpu_baseline(name, score_rows, attn_rows):
     total = t_score + t_select + t_gather + t_attn
     measured = t_score * (len(rows) / w.n) + t_select + t_gather + t_attn_sample
     return {"value": w.n / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", "cpu_model": cpu_model(),
+            "host_cores_available": _HOST_CORES,
+            "blas_threads_env": {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")},
             "sample": (f"{name}: gate score on {len(rows)} of {w.n} rows, full select and gather, "
                        f"attention on {len(arows)} of {m} query rows"
                        + ("" if len(rows) == w.n and len(arows) == m else
@@ -469,27 +493,31 @@ def main():
     sec_cold = path.timed_cold(max(5, args.steps // 2))
     w = path.w
     alg = algorithmic(w, path.k)
-    attn_tflops = alg["attn_flops"] / (stage_mean[3] * 1e-6) / 1e12
-    sel_gather_gbs = (alg["select_bytes"] + alg["gather_bytes"]) / ((stage_mean[1] + stage_mean[2]) * 1e-6) / 1e9
+    attn_tflops = alg["attn_flops"] / (stage_mean[2] * 1e-6) / 1e12
+    sel_gather_gbs = alg["select_gather_bytes"] / (stage_mean[1] * 1e-6) / 1e9
     score_gbs = alg["score_bytes"] / (stage_mean[0] * 1e-6) / 1e9
     score_tflops = alg["score_flops"] / (stage_mean[0] * 1e-6) / 1e12
     print(f"[bench] {args.workload}: {sec * 1e3:.3f} ms/step (graph), {sec_eager * 1e3:.3f} eager; "
-          f"stages us (mean) score {stage_mean[0]:.1f} "
-          f"select {stage_mean[1]:.1f} gather {stage_mean[2]:.1f} attention {stage_mean[3]:.1f}",
-          file=sys.stderr, flush=True)
+          f"stages us (mean) score {stage_mean[0]:.1f} select+gather {stage_mean[1]:.1f} "
+          f"attention {stage_mean[2]:.1f}", file=sys.stderr, flush=True)
 
-    also = None
-    if args.also and args.also != args.workload:
-        p2 = Path(args.also, binding, torch)
+    also = []
+    for name in [a for a in args.also.split(",") if a and a != args.workload]:
+        p2 = Path(name, binding, torch)
         _, st2, st2m = p2.timed(args.steps, args.warmup)
         sec2e = p2.eager_period
         sec2 = p2.timed_graph(args.steps, args.warmup)
         sec2c = p2.timed_cold(max(5, args.steps // 2))
-        also = {"workload": args.also, "tokens_per_s": p2.w.n / sec2, "ms_per_step": sec2 * 1e3,
-                "cold_ms_per_step": sec2c * 1e3, "cold_tokens_per_s": p2.w.n / sec2c,
-                "eager_ms_per_step": sec2e * 1e3, "eager_tokens_per_s": p2.w.n / sec2e,
-                "stage_us_mean": {"score": st2[0], "select": st2[1], "gather": st2[2], "attention": st2[3]},
-                "stage_us_median": {"score": st2m[0], "select": st2m[1], "gather": st2m[2], "attention": st2m[3]}}
+        alg2 = algorithmic(p2.w, p2.k)
+        also.append({"workload": name, "n": p2.w.n, "k": p2.k, "m": p2.m, "tokens_per_s": p2.w.n / sec2,
+                     "ms_per_step": sec2 * 1e3, "cold_ms_per_step": sec2c * 1e3, "cold_tokens_per_s": p2.w.n / sec2c,
+                     "eager_ms_per_step": sec2e * 1e3, "eager_tokens_per_s": p2.w.n / sec2e,
+                     "stage_us_mean": dict(zip(STAGES, (float(v) for v in st2))),
+                     "stage_us_median": dict(zip(STAGES, (float(v) for v in st2m))),
+                     "attention_frac_mfma_peak": alg2["attn_flops"] / (st2[2] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                     "select_gather_frac_hbm_peak": alg2["select_gather_bytes"] / (st2[1] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                     "score_frac_hbm_peak": alg2["score_bytes"] / (st2[0] * 1e-6) / 1e9 / PEAK_HBM_GBS})
+        print(f"[bench] {name}: {sec2 * 1e3:.3f} ms/step (graph)", file=sys.stderr, flush=True)
         del p2
         torch.cuda.empty_cache()
 
@@ -518,8 +546,11 @@ def main():
         "ms_per_step": sec * 1e3,
         "eager_ms_per_step": sec_eager * 1e3,
         "cold_ms_per_step": sec_cold * 1e3,
-        "step_launch": "HIP graph of the step's four launches, replayed back to back; eager steps give the "
-                       "stage times; cold = median replay after a 1 GiB fill that evicts L2 and the Infinity Cache",
+        "step_launch": "HIP graph of the step's three launches (score, select+gather, attention), replayed back "
+                       "to back; eager steps give the stage times",
+        "value_cache_state": "warm: back-to-back replays, nothing flushed between them (X of the 128k workload, "
+                             "512 MiB, exceeds the 256 MB Infinity Cache anyway); cold_ms_per_step = median "
+                             "replay after a 1 GiB fill that evicts L2 and the Infinity Cache",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -533,19 +564,22 @@ def main():
                      "traffic": attention_traffic(w.name)},
         "cpu_baseline": cpu,
         "stages": {
-            "us_mean": {"score": stage_mean[0], "select": stage_mean[1], "gather": stage_mean[2],
-                        "attention": stage_mean[3]},
-            "us_median": {"score": stage_med[0], "select": stage_med[1], "gather": stage_med[2],
-                          "attention": stage_med[3]},
+            "us_mean": dict(zip(STAGES, (float(v) for v in stage_mean))),
+            "us_median": dict(zip(STAGES, (float(v) for v in stage_med))),
             "attention_tflops": attn_tflops, "attention_frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS,
             "select_gather_gbs": sel_gather_gbs, "select_gather_frac_hbm_peak": sel_gather_gbs / PEAK_HBM_GBS,
+            "select_gather_bytes": alg["select_gather_bytes"],
             "score_gbs": score_gbs, "score_frac_hbm_peak": score_gbs / PEAK_HBM_GBS, "score_tflops": score_tflops,
         },
         "also": also,
         "next_rows": nxt,
         "sweep64k": sweep,
     }
-    print(json.dumps(out))
+    print(json.dumps(out), flush=True)
+    # release device memory while the runtime is fully up, before interpreter teardown
+    del path
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return 0
 
 

@@ -55,6 +55,7 @@ extern "C" {
 #define TG_ERR_UNSUPPORTED 2   /* a shape or alignment this library has no kernel for */
 #define TG_ERR_WORKSPACE   3   /* workspace too small */
 #define TG_ERR_HIP         4   /* the HIP runtime reported an error at launch */
+#define TG_ERR_INCOMPLETE  5   /* tg_select_check: a selection gave up waiting (see there) */
 
 typedef int32_t tg_status;
 
@@ -82,7 +83,7 @@ const char* tg_status_string(tg_status status);
  *   scores    [n] float32 output
  * Arithmetic: bf16 operands with float32 accumulation (MFMA); GELU and the
  * 1-wide output dot in float32.  f32: float32 throughout.
- * Supported: n in [1, 2^31-1].  bf16: d_model % 64 == 0, d_hidden in {64, 128, 256},
+ * Supported: n in [1, 2^31-1].  bf16: d_model % 64 == 0, d_hidden in {64, 128, 192, 256},
  * ldx % 8 == 0, x and w1 16-byte aligned.  f32: d_model % 4 == 0, ldx % 4 == 0,
  * d_hidden in [1, 256].  Otherwise TG_ERR_UNSUPPORTED.
  */
@@ -99,7 +100,9 @@ tg_status tg_gate_score(int32_t dtype, int64_t n, int32_t d_model, int32_t d_hid
  */
 int64_t tg_num_kept(int64_t n, int64_t doc_begin, int64_t doc_end, int64_t k);
 
-/* Bytes of workspace tg_select_topk needs for n scores (host only); 0 if n < 0. */
+/* Bytes of workspace the selection calls need for n scores (host only); 0 if n < 0.  One
+ * workspace serves tg_select_topk, tg_select_gather, tg_select_topk_multi and
+ * tg_select_random. */
 size_t tg_select_workspace_bytes(int64_t n);
 
 /*
@@ -114,14 +117,51 @@ size_t tg_select_workspace_bytes(int64_t n);
  *   kept_idx   [m] int32 output
  *   workspace  >= tg_select_workspace_bytes(n) bytes, 256-byte aligned.  It must be
  *              zero-filled before its first use; every call leaves the parts that
- *              must start at zero (digit histograms, done counters) at zero again,
- *              so a workspace can be reused for any n it is large enough for.
+ *              must start at zero (histograms, counters, flags) at zero again, so a
+ *              workspace can be reused for any n it is large enough for.
+ * The selection is one launch whose workgroups wait for each other; every wait is
+ * bounded.  If a wait gives up (possible only when other work occupies the device so
+ * that not all of the launch's workgroups are resident at once), or if the call finds
+ * the workspace not zero-filled, the workspace's sticky failure word is set, the
+ * outputs are invalid, and every later selection on that workspace exits without
+ * writing until the caller zero-fills it again; tg_select_check reports the word.
+ * Test hook: a non-zero uint32 at byte offset 12 of the workspace bounds each wait to
+ * that many polls; 0xFFFFFFFF makes every wait give up at once (a zero-filled
+ * workspace waits up to 2^22 polls).
  * m = 0 (the whole prompt is a document and k = 0) is a no-op.
  * Supported: n in [1, 2^31-1].
  */
 tg_status tg_select_topk(int64_t n, const float* scores, int64_t doc_begin, int64_t doc_end,
                          int64_t k, int32_t* kept_idx, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/*
+ * tg_select_gather -- tg_select_topk and tg_gather_kept in one launch: the kept
+ * positions, the kept rows of x and their scores (aiproducthub.cn, section 事件详情:
+ * the top-K selector keeps the best tokens and layers above the gate see only those;
+ * aisight.pl, section "Jak to dziala").
+ *     kept_idx[r] = r-th kept position (ascending),   x_kept[r, :] = x[kept_idx[r], :],
+ *     s_kept[r] = scores[kept_idx[r]]                 (r < m = tg_num_kept(n, ..., k))
+ *   dtype      TG_F32 or TG_BF16: element type of x and x_kept
+ *   x          [n, d_model], row stride ldx >= d_model
+ *   x_kept     [m, d_model] output, row stride ld_out >= d_model
+ *   s_kept     [m] float32 output (required)
+ * Selection, workspace, failure reporting and errors as tg_select_topk; the copy is
+ * bit-exact.  m = 0 is a no-op.
+ */
+tg_status tg_select_gather(int32_t dtype, int64_t n, int32_t d_model, const float* scores,
+                           int64_t doc_begin, int64_t doc_end, int64_t k, const void* x, int64_t ldx,
+                           int32_t* kept_idx, void* x_kept, int64_t ld_out, float* s_kept,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tg_select_check -- whether every selection enqueued so far on `workspace` completed.
+ * Synchronises `stream` (the host blocks until the stream's work is done), then reads
+ * the workspace's sticky failure word: TG_OK if it is clear; TG_ERR_INCOMPLETE if a
+ * selection gave up waiting or found the workspace not zero-filled (its outputs are
+ * invalid; zero-fill the workspace before reusing it); TG_ERR_HIP on a runtime error.
+ */
+tg_status tg_select_check(const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * tg_select_topk_multi -- tg_select_topk for several budgets of the same scores in one
@@ -223,12 +263,10 @@ tg_status tg_gated_attention_lse(int32_t dtype, int64_t m, int32_t n_q_heads, in
  *     (no workspace);
  *   - runs: each query tile's key tiles are cut into runs of split_tiles, walked by
  *     different workgroups; every run writes its partial softmax state to the workspace
- *     (its normalised output row Y_j = O_j / l_j in float16, its running max m_j and row
- *     sum l_j in float32) and a second kernel combines the runs of a row: w_j = 2^(m_j - M)
- *     l_j with M = max m_j, out = sum w_j Y_j / sum w_j, in run order (deterministic).
- *     Query tiles with one run are written directly.  The float16 rows add at most 2^-11
- *     relative rounding to the output and require |v| < 65504 (the largest float16) where
- *     runs occur.
+ *     (its normalised output row Y_j = O_j / l_j, its running max m_j and row sum l_j, all
+ *     float32) and a second kernel combines the runs of a row: w_j = 2^(m_j - M) l_j with
+ *     M = max m_j, out = sum w_j Y_j / sum w_j, in run order (deterministic).  Query tiles
+ *     with one run are written directly.
  *   split_tiles  0: chosen by the library: with at most 768 workgroups of query tiles and
  *                at least 4 head slots each, key groups; with fewer head slots, runs of
  *                max(8, ceil(total key-tile work / 256)) tiles (key groups if that is not
@@ -313,6 +351,23 @@ tg_status tg_qkv_rope(int32_t dtype, int64_t m, int32_t d_model, const void* x_k
                       int32_t head_dim, const int32_t* pos, float rope_theta, void* q_out, void* k_cache,
                       void* v_cache, int32_t* pos_cache, int64_t cache_slot0, int64_t cache_capacity,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * tg_check_positions -- the attention's precondition on pos (kept tokens keep their order
+ * and the causal mask is on original positions: aiproducthub.cn, section 事件详情):
+ *     *violations = #{i in [1, m) : pos[i] <= pos[i-1]} + #{i : pos[i] < 0}
+ *   pos         [m] int32 (device)
+ *   violations  one int32 (device), written (not accumulated); 0 means pos is strictly
+ *               increasing and non-negative
+ * One workgroup; asynchronous like every call.  TG_ERR_INVALID_ARG for m < 0 or a NULL
+ * pointer (pos may be NULL when m == 0).
+ */
+tg_status tg_check_positions(const int32_t* pos, int64_t m, int32_t* violations, void* stream);
+
+/* 1 if this library was built with TG_DEBUG: then tg_gated_attention, _lse, _split and
+ * _backward run tg_check_positions on pos first, synchronise the stream, and return
+ * TG_ERR_INVALID_ARG (nothing else enqueued) if pos is not strictly increasing. */
+int32_t tg_debug_build(void);
 
 #ifdef __cplusplus
 }

@@ -8,6 +8,7 @@ import fails loudly.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 
@@ -51,6 +52,14 @@ _lib.tg_select_topk.restype = _i32
 _lib.tg_select_topk.argtypes = [_i64, _p, _i64, _i64, _i64, _p, _p, _sz, _p]
 _lib.tg_select_topk_multi.restype = _i32
 _lib.tg_select_topk_multi.argtypes = [_i64, _p, _i64, _i64, ctypes.POINTER(ctypes.c_int64), _i32, _p, _p, _sz, _p]
+_lib.tg_select_gather.restype = _i32
+_lib.tg_select_gather.argtypes = [_i32, _i64, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _sz, _p]
+_lib.tg_select_check.restype = _i32
+_lib.tg_select_check.argtypes = [_p, _sz, _p]
+_lib.tg_check_positions.restype = _i32
+_lib.tg_check_positions.argtypes = [_p, _i64, _p, _p]
+_lib.tg_debug_build.restype = _i32
+_lib.tg_debug_build.argtypes = []
 _lib.tg_select_random.restype = _i32
 _lib.tg_select_random.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_uint64, _p, _p, _sz, _p]
 _lib.tg_gather_kept.restype = _i32
@@ -153,18 +162,44 @@ def tg_gate_score(x, w1, w2, b1=None, b2: float = 0.0, out=None, stream=None):
     return out
 
 
+# Cached selection workspaces, one per (device, stream): calls that share a workspace must
+# not run concurrently, and calls on one stream never do.
 _workspaces = {}
 
 
-def select_workspace(n: int, device) -> torch.Tensor:
-    """Cached, zero-filled selection workspace for `device` with room for n scores."""
+def _release_workspaces():
+    """Drops the cached device buffers while the runtime is still up (interpreter exit runs
+    this before module teardown, so no device memory is released after the HIP runtime)."""
+    _workspaces.clear()
+
+
+atexit.register(_release_workspaces)
+
+
+def select_workspace(n: int, device, stream=None) -> torch.Tensor:
+    """Cached, zero-filled selection workspace for `device` and `stream` (default: the
+    device's current stream) with room for n scores."""
     need = tg_select_workspace_bytes(n)
-    key = torch.device(device)
+    dev = torch.device(device)
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    key = (dev, int(s.cuda_stream))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.zeros(max(need, 1 << 16), dtype=torch.uint8, device=key)
+        ws = torch.zeros(max(need, 1 << 16), dtype=torch.uint8, device=dev)
+        cur = torch.cuda.current_stream(dev)
+        if int(cur.cuda_stream) != int(s.cuda_stream):
+            s.wait_stream(cur)   # the zero-fill ran on the current stream
         _workspaces[key] = ws
     return ws
+
+
+def tg_select_check(workspace, stream=None):
+    """Synchronises the stream and raises TokenGateError (TG_ERR_INCOMPLETE) if a selection
+    on `workspace` gave up waiting or found it not zero-filled: its outputs are then invalid
+    and the workspace must be zero-filled again."""
+    dev = _on_gpu(workspace)
+    _check("tg_select_check", _lib.tg_select_check(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                   _stream(dev, stream)))
 
 
 def tg_select_topk(scores, doc_begin: int, doc_end: int, k: int, out=None, workspace=None, stream=None):
@@ -180,11 +215,43 @@ def tg_select_topk(scores, doc_begin: int, doc_end: int, k: int, out=None, works
         out = torch.empty(m, dtype=torch.int32, device=dev)
     elif out.dtype != torch.int32 or out.numel() < m or not out.is_contiguous():
         raise ValueError("out must be a contiguous int32 tensor with room for m entries")
-    ws = workspace if workspace is not None else select_workspace(n, dev)
+    ws = workspace if workspace is not None else select_workspace(n, dev, stream)
     _check("tg_select_topk", _lib.tg_select_topk(
         n, _ptr(scores), doc_begin, doc_end, k, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(dev, stream)))
     return out[:m]
+
+
+def tg_select_gather(scores, x, doc_begin: int, doc_end: int, k: int, kept=None, x_kept=None, s_kept=None,
+                     workspace=None, stream=None):
+    """tg_select_topk and tg_gather_kept in one launch -> (kept int32 [m], x_kept [m, d_model], s_kept [m])."""
+    dev = _on_gpu(scores, x, kept, x_kept, s_kept, workspace)
+    if scores.dtype != torch.float32 or scores.dim() != 1 or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 vector")
+    if x.dim() != 2 or x.stride(1) != 1 or x.shape[0] != scores.shape[0]:
+        raise ValueError("x must be [n, d_model] with unit column stride, one row per score")
+    n, d_model = x.shape
+    m = tg_num_kept(n, doc_begin, doc_end, k)
+    if m < 0:
+        raise ValueError("invalid document span or budget")
+    if kept is None:
+        kept = torch.empty(max(m, 1), dtype=torch.int32, device=dev)
+    elif kept.dtype != torch.int32 or kept.numel() < m or not kept.is_contiguous():
+        raise ValueError("kept must be a contiguous int32 tensor with room for m entries")
+    if x_kept is None:
+        x_kept = torch.empty(max(m, 1), d_model, dtype=x.dtype, device=dev)
+    elif x_kept.dtype != x.dtype or x_kept.shape[0] < m or x_kept.shape[1] != d_model or x_kept.stride(1) != 1:
+        raise ValueError("x_kept must be [>= m, d_model] of x's dtype")
+    if s_kept is None:
+        s_kept = torch.empty(max(m, 1), dtype=torch.float32, device=dev)
+    elif s_kept.dtype != torch.float32 or s_kept.numel() < m or not s_kept.is_contiguous():
+        raise ValueError("s_kept must be a contiguous float32 tensor with room for m entries")
+    ws = workspace if workspace is not None else select_workspace(n, dev, stream)
+    _check("tg_select_gather", _lib.tg_select_gather(
+        _dtype_code(x), n, d_model, _ptr(scores), doc_begin, doc_end, k, _ptr(x), x.stride(0), _ptr(kept),
+        _ptr(x_kept), x_kept.stride(0), _ptr(s_kept), _ptr(ws), ws.numel() * ws.element_size(),
+        _stream(dev, stream)))
+    return kept[:m], x_kept[:m], s_kept[:m]
 
 
 def tg_select_topk_multi(scores, doc_begin: int, doc_end: int, ks, out=None, workspace=None, stream=None):
@@ -202,7 +269,7 @@ def tg_select_topk_multi(scores, doc_begin: int, doc_end: int, ks, out=None, wor
         out = torch.empty(max(total, 1), dtype=torch.int32, device=dev)
     elif out.dtype != torch.int32 or out.numel() < total or not out.is_contiguous():
         raise ValueError("out must be a contiguous int32 tensor with room for every kept list")
-    ws = workspace if workspace is not None else select_workspace(n, dev)
+    ws = workspace if workspace is not None else select_workspace(n, dev, stream)
     karr = (ctypes.c_int64 * len(ks))(*ks)
     _check("tg_select_topk_multi", _lib.tg_select_topk_multi(
         n, _ptr(scores), doc_begin, doc_end, karr, len(ks), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
@@ -224,7 +291,7 @@ def tg_select_random(n: int, doc_begin: int, doc_end: int, k: int, seed: int, de
         out = torch.empty(max(m, 1), dtype=torch.int32, device=dev)
     elif out.dtype != torch.int32 or out.numel() < m or not out.is_contiguous():
         raise ValueError("out must be a contiguous int32 tensor with room for m entries")
-    ws = workspace if workspace is not None else select_workspace(n, dev)
+    ws = workspace if workspace is not None else select_workspace(n, dev, stream)
     _check("tg_select_random", _lib.tg_select_random(
         n, doc_begin, doc_end, k, seed & 0xFFFFFFFFFFFFFFFF, _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(dev, stream)))
@@ -253,6 +320,18 @@ def tg_gather_kept(x, kept_idx, scores=None, out=None, s_out=None, stream=None):
         _dtype_code(x), n, d_model, _ptr(x), x.stride(0), _ptr(kept_idx), m, _ptr(out), out.stride(0),
         _ptr(scores), _ptr(s_out if scores is not None else None), _stream(dev, stream)))
     return out[:m], (s_out[:m] if scores is not None else None)
+
+
+def tg_check_positions(pos, out=None, stream=None):
+    """Number of positions that break "strictly increasing and non-negative" (a device int32
+    tensor of one element; `.item()` synchronises)."""
+    dev = _on_gpu(pos, out)
+    if pos.dtype != torch.int32 or pos.dim() != 1 or not pos.is_contiguous():
+        raise ValueError("pos must be a contiguous int32 vector")
+    if out is None:
+        out = torch.empty(1, dtype=torch.int32, device=dev)
+    _check("tg_check_positions", _lib.tg_check_positions(_ptr(pos), pos.shape[0], _ptr(out), _stream(dev, stream)))
+    return out
 
 
 def _check_attention_args(q, k, v, pos, s_kept, gain):

@@ -18,7 +18,11 @@ ROOT = os.path.dirname(HERE)
 LIB_NAME = "libtokengate.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["tg_api.hip", "tg_score.hip", "tg_select.hip", "tg_gather.hip", "tg_attention.hip",
-           "tg_attention_bwd.hip", "tg_qkv.hip"]
+           "tg_attention_bwd.hip", "tg_qkv.hip", "tg_check.hip"]
+# The debug library: the same sources with TG_DEBUG, whose attention entry points also
+# check that pos is strictly increasing (synchronising the stream) before launching.
+DEBUG_LIB_NAME = "libtokengate_debug.so"
+DEBUG_LIB_PATH = os.path.join(HERE, DEBUG_LIB_NAME)
 ARCH = "gfx950"
 # Per-source extra flags.  The attention kernel's inputs are finite by contract; without
 # NaN semantics the compiler does not re-canonicalise every MFMA result before taking a
@@ -50,24 +54,32 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    obj_dir = os.path.join(HERE, "_build")
+def _build_lib(cc, obj_dir, lib_path, defines):
     os.makedirs(obj_dir, exist_ok=True)
-    cc = hipcc()
 
     def compile_one(src):
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
-        _run([cc, *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+        _run([cc, *common_flags(), *defines, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 
     workers = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "8"))))
     with ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Builds libtokengate.so and (debug=True) libtokengate_debug.so; returns the first's path."""
+    cc = hipcc()
+    _build_lib(cc, os.path.join(HERE, "_build"), LIB_PATH, [])
     if verbose:
         print(f"built {LIB_PATH}")
+    if debug:
+        _build_lib(cc, os.path.join(HERE, "_build", "debug"), DEBUG_LIB_PATH, ["-DTG_DEBUG"])
+        if verbose:
+            print(f"built {DEBUG_LIB_PATH}")
     return LIB_PATH
 
 

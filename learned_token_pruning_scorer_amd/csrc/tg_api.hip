@@ -10,6 +10,9 @@ extern "C" const char* tg_status_string(tg_status status) {
     case TG_ERR_UNSUPPORTED: return "TG_ERR_UNSUPPORTED: shape or alignment not supported by this library";
     case TG_ERR_WORKSPACE: return "TG_ERR_WORKSPACE: workspace too small";
     case TG_ERR_HIP: return "TG_ERR_HIP: HIP runtime error at launch";
+    case TG_ERR_INCOMPLETE:
+      return "TG_ERR_INCOMPLETE: a selection on this workspace gave up waiting for its workgroups (or found the "
+             "workspace not zero-filled); its outputs are invalid and the workspace must be zero-filled again";
     default: return "unknown tg_status";
   }
 }

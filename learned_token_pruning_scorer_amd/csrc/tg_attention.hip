@@ -124,11 +124,11 @@ struct AttnCfg {
 // Key split: query tile qt's key tiles are cut into runs of `tiles`; run j (grid y) walks
 // tiles [j tiles, (j + 1) tiles).  Query tiles with more than one run (qt >= qt0) write
 // partial states: part_o [qt - qt0][j][row in tile][head][D], the run's normalised output
-// row O_j / l_j in float16, and part_ml (same index) = [m_j, l_j] in float32; tiles = 0
+// row O_j / l_j in float32, and part_ml (same index) = [m_j, l_j] in float32; tiles = 0
 // means no split.
 struct AttnSplit {
   int tiles, qt0, jmax;
-  _Float16* part_o;
+  float* part_o;
   float* part_ml;
 };
 
@@ -456,24 +456,23 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
 
   const float l_tot = pair_sum(l_run + l_run2);
   if (RUNS && to_part) {
-    // one run of a query tile: the run's normalised output row (float16), its running max
+    // one run of a query tile: the run's normalised output row (float32), its running max
     // (base-2 units) and row sum go to the workspace; attn_merge_kernel combines the runs.
     // A wave that saw no key of this run leaves l = 0, which the merge skips.
     if (row < m) {
       const int64_t prow =
           ((int64_t)((qt - sp.qt0) * sp.jmax + (int)blockIdx.y) * C::ROWS + (row - qt * C::ROWS)) * hq + head;
-      _Float16* po = sp.part_o + prow * D;
+      float* po = sp.part_o + prow * D;
       const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-      typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
       for (int u = 0; u < D / 32; ++u)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int d0 = 32 * u + 8 * g + 4 * half;
-          f16x4 o4;
+          f32x4 o4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o4[e] = static_cast<_Float16>(oacc[u][4 * g + e] * inv);
-          *reinterpret_cast<f16x4*>(po + d0) = o4;
+          for (int e = 0; e < 4; ++e) o4[e] = oacc[u][4 * g + e] * inv;
+          *reinterpret_cast<f32x4*>(po + d0) = o4;
         }
       if (half == 0) {
         typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -522,7 +521,6 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int m, int hq, int rows
   const int64_t base = ((int64_t)(qt - sp.qt0) * sp.jmax * rows + (row - qt * rows)) * hq + head;
   const int64_t jstride = (int64_t)rows * hq;
   typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
   // runs are read JC at a time, every load of a group issued before any is used
   constexpr int JC = 8;
   float mx = -INFINITY;
@@ -540,12 +538,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int m, int hq, int rows
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int j0 = 0; j0 < nj; j0 += JC) {
     f32x2 ml[JC];
-    f16x4 y[JC];
+    f32x4 y[JC];
 #pragma unroll
     for (int c = 0; c < JC; ++c) {
       const int64_t pr = base + (j0 + c) * jstride;
       ml[c] = j0 + c < nj ? *reinterpret_cast<const f32x2*>(sp.part_ml + pr * 2) : f32x2{0.f, 0.f};
-      y[c] = j0 + c < nj ? *reinterpret_cast<const f16x4*>(sp.part_o + pr * D + d0) : f16x4{};
+      y[c] = j0 + c < nj ? *reinterpret_cast<const f32x4*>(sp.part_o + pr * D + d0) : f32x4{};
     }
 #pragma unroll
     for (int c = 0; c < JC; ++c) {
@@ -553,7 +551,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(int m, int hq, int rows
       const float w = __builtin_amdgcn_exp2f(ml[c][0] - mx) * ml[c][1];
       l += w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, static_cast<float>(y[c][e]), acc[e]);
+      for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, y[c][e], acc[e]);
     }
   }
   const float inv = 1.0f / l;
@@ -613,7 +611,7 @@ static AttnPlan plan_attn(int m, int hq, int hkv, int head_dim, int split_tiles)
   p.qt0 = 0;
   while (n_tiles(p.qt0) <= tiles) ++p.qt0;
   const size_t prow = (size_t)(p.n_qtiles - p.qt0) * p.jmax * p.rows * hq;
-  p.part_o_bytes = (prow * head_dim * 2 + 255) & ~size_t(255);
+  p.part_o_bytes = (prow * head_dim * 4 + 255) & ~size_t(255);
   p.part_ml_bytes = (prow * 2 * 4 + 255) & ~size_t(255);
   return p;
 }
@@ -764,6 +762,9 @@ static tg_status gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, in
   if (lse && dtype != TG_BF16) return TG_ERR_UNSUPPORTED;
   if (m == 0) return TG_OK;
   if (!q || !k || !v || !out) return TG_ERR_INVALID_ARG;
+#ifdef TG_DEBUG
+  if (const tg_status s = debug_check_positions(pos, m, stream); s != TG_OK) return s;
+#endif
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out);
   if (align & 15u) return TG_ERR_UNSUPPORTED;
@@ -777,7 +778,7 @@ static tg_status gated_attention(int32_t dtype, int64_t m, int32_t n_q_heads, in
     if (p.tiles > 0) {
       if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return TG_ERR_INVALID_ARG;
       if (workspace_bytes < p.part_o_bytes + p.part_ml_bytes) return TG_ERR_WORKSPACE;
-      sp.part_o = static_cast<_Float16*>(workspace);
+      sp.part_o = static_cast<float*>(workspace);
       sp.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_o_bytes);
     }
     return head_dim == 128

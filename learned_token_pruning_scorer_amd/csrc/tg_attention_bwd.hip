@@ -27,13 +27,14 @@
 //         query), and dQ^T += K^T dZ^T reads K^T from the tile with ds_read_b64_tr_b16;
 //  * dkv: the transpose, on 16x16x32 MFMA -- a workgroup (8 waves, two per SIMD) owns
 //         128 keys of one key/value head and a wave 16 of them, with K and V as fixed B
-//         operands in registers and the dK / dV accumulators beside them (about 120
-//         registers, so two waves share a SIMD and hide each other's latencies);
+//         operands in registers and the dK / dV accumulators beside them (about 220
+//         registers with the compiler's prefetching, which still lets two waves share
+//         a SIMD and hide each other's latencies);
 //         32-query Q / dO tiles of every head of the group stream through a 3-stage LDS
 //         ring; S = Q K^T and dP = dO V^T give P and dZ (lane = key), dV^T += dO^T P and
 //         dK^T += Q^T dZ read dO^T and Q^T from the tiles by transposing LDS reads.  The
 //         key-side sums (ds, dgain, dtau) accumulate per lane and leave as
-//         per-workgroup partials;
+//         per-wave partials;
 //  * reduce: sums the partials of ds (over key/value heads), dgain and dtau in a fixed
 //         order, so results are deterministic.
 // Every gradient element is written by exactly one workgroup: no float atomics.
@@ -635,6 +636,9 @@ extern "C" tg_status tg_gated_attention_backward(int32_t dtype, int64_t m, int32
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !workspace) return TG_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return TG_ERR_INVALID_ARG;
   if (workspace_bytes < BwdLayout(m, n_q_heads, n_kv_heads).bytes) return TG_ERR_WORKSPACE;
+#ifdef TG_DEBUG
+  if (const tg_status s = debug_check_positions(pos, m, stream); s != TG_OK) return s;
+#endif
   const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
                           reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(out) |
                           reinterpret_cast<uintptr_t>(dout) | reinterpret_cast<uintptr_t>(dq) |

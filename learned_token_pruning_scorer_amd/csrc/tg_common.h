@@ -100,6 +100,12 @@ __device__ __forceinline__ void dma_lds4(uint32_t off, const void* base, uint32_
 // Wait until every DMA (and any other vector memory access) this wave issued has landed.
 __device__ __forceinline__ void dma_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+#ifdef TG_DEBUG
+// Debug builds: counts the violations of "pos strictly increasing and non-negative" on the
+// stream, synchronises it, and returns TG_ERR_INVALID_ARG if there is any (tg_check.hip).
+tg_status debug_check_positions(const int32_t* pos, int64_t m, void* stream);
+#endif
+
 }  // namespace tg
 
 #define TG_CHECK_LAUNCH()                                   \

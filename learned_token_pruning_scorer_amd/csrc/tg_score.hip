@@ -100,7 +100,8 @@ constexpr int kScorePitch = kScoreKC + 8; // LDS row pitch in bf16 (144 B: confl
 template <int H, int BTW>
 struct ScoreTile {
   static constexpr int HT = H / 32;               // 32-row hidden tiles in total
-  static constexpr int AT = HT < 4 ? HT : 4;      // hidden tiles per wave
+  // hidden tiles per wave: 4 where they divide evenly (128, 256), 3 for 192, else all
+  static constexpr int AT = HT % 4 == 0 ? 4 : (HT % 3 == 0 ? 3 : HT);
   static constexpr int WH = HT / AT;              // waves along hidden
   static constexpr int WT = kScoreWaves / WH;     // waves along tokens
   static constexpr int BT = 32 * BTW * WT;        // tokens per workgroup
@@ -448,13 +449,15 @@ extern "C" tg_status tg_gate_score(int32_t dtype, int64_t n, int32_t d_model, in
   // fill the chip, which halves the W1 re-reads per token, else 128-token tiles (three
   // stages), and 64-token tiles (4 waves along the hidden units) below 32768 tokens, where
   // 128-token tiles leave CUs idle.  The row offsets of one tile must fit 32 bits.
-  // 64/128: register-staged tiles.
+  // 64/128/192: register-staged tiles.
   const bool big = n >= 65536, small = n < 32768;
   switch (d_hidden) {
     case 64:
       return launch_score_bf16<64, 1>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
     case 128:
       return launch_score_bf16<128, 1>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
+    case 192:
+      return launch_score_bf16<192, 1>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);
     case 256:
       if ((int64_t)ldx * 2 * 256 > INT32_MAX || (int64_t)d_model * 2 * 256 > INT32_MAX) return TG_ERR_UNSUPPORTED;
       if (big) return launch_score_ring<2, 2>(nn, d_model, x, ldx, w1, b1, w2, b2, scores, st);

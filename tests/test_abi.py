@@ -38,6 +38,8 @@ def lib():
     lib.tg_select_workspace_bytes.argtypes = [i64]
     lib.tg_gate_score.argtypes = [i32, i64, i32, i32, p, i64, p, p, p, f32, p, p]
     lib.tg_select_topk.argtypes = [i64, p, i64, i64, i64, p, p, sz, p]
+    lib.tg_select_gather.argtypes = [i32, i64, i32, p, i64, i64, i64, p, i64, p, p, i64, p, p, sz, p]
+    lib.tg_select_check.argtypes = [p, sz, p]
     lib.tg_gather_kept.argtypes = [i32, i64, i32, p, i64, p, i64, p, i64, p, p, p]
     lib.tg_gated_attention.argtypes = [i32, i64, i32, i32, i32, p, p, p, p, p, p, f32, p, p]
     lib.tg_select_topk_multi.argtypes = [i64, p, i64, i64, ctypes.POINTER(i64), i32, p, p, sz, p]
@@ -65,7 +67,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.tg_abi_version() == 1
-    for code in range(5):
+    for code in range(6):
         assert lib.tg_status_string(code).startswith(b"TG_")
     assert lib.tg_status_string(99) == b"unknown tg_status"
 
@@ -115,6 +117,54 @@ def test_select_validation(lib):
     assert lib.tg_select_topk(1000, FAKE, 0, 900, 10, FAKE, ws, need - 1, None) == TG_ERR_WORKSPACE
     # nothing kept (all document, k = 0): a no-op that succeeds without any pointer
     assert lib.tg_select_topk(1000, None, 0, 1000, 0, None, None, 0, None) == TG_OK
+
+
+def test_select_gather_validation(lib):
+    ws = ctypes.c_void_p(1 << 20)
+    need = lib.tg_select_workspace_bytes(1000)
+    ok = dict(dtype=1, n=1000, d=64, s=FAKE, b=0, e=900, k=10, x=FAKE, ldx=64, kept=FAKE, xk=FAKE, ldo=64, sk=FAKE,
+              ws=ws, need=need)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.tg_select_gather(a["dtype"], a["n"], a["d"], a["s"], a["b"], a["e"], a["k"], a["x"], a["ldx"],
+                                    a["kept"], a["xk"], a["ldo"], a["sk"], a["ws"], a["need"], None)
+    assert call(x=None) == TG_ERR_INVALID_ARG
+    assert call(sk=None) == TG_ERR_INVALID_ARG
+    assert call(xk=None) == TG_ERR_INVALID_ARG
+    assert call(s=None) == TG_ERR_INVALID_ARG
+    assert call(kept=None) == TG_ERR_INVALID_ARG
+    assert call(dtype=3) == TG_ERR_INVALID_ARG
+    assert call(ldx=32) == TG_ERR_INVALID_ARG
+    assert call(ldo=32) == TG_ERR_INVALID_ARG
+    assert call(d=0) == TG_ERR_INVALID_ARG
+    assert call(b=901) == TG_ERR_INVALID_ARG
+    assert call(k=-1) == TG_ERR_INVALID_ARG
+    assert call(n=0) == TG_ERR_INVALID_ARG
+    assert call(ws=ctypes.c_void_p((1 << 20) + 4)) == TG_ERR_INVALID_ARG
+    assert call(need=need - 1) == TG_ERR_WORKSPACE
+    # nothing kept: a no-op
+    assert call(e=1000, k=0, s=None, kept=None, ws=None, need=0) == TG_OK
+
+
+def test_select_check_validation(lib):
+    assert lib.tg_select_check(None, 1 << 20, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_select_check(FAKE, 8, None) == TG_ERR_INVALID_ARG
+
+
+def test_check_positions_validation_and_debug_flag(lib):
+    lib.tg_check_positions.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.tg_check_positions(FAKE, -1, FAKE, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_check_positions(FAKE, 10, None, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_check_positions(None, 10, FAKE, None) == TG_ERR_INVALID_ARG
+    assert lib.tg_debug_build() == 0
+    dbg_path = os.path.join(ROOT, "learned_token_pruning_scorer_amd", "libtokengate_debug.so")
+    if not os.path.exists(dbg_path):
+        pytest.fail("libtokengate_debug.so is not built (python -m learned_token_pruning_scorer_amd.build)")
+    dbg = ctypes.CDLL(dbg_path, mode=os.RTLD_NOW)
+    assert dbg.tg_debug_build() == 1
+    for name in declared_functions():
+        assert hasattr(dbg, name), name
 
 
 def test_gather_validation(lib):
@@ -200,7 +250,7 @@ def test_attention_lse_and_backward_validation(lib):
 
 
 def split_plan_bytes(m, hq, hkv, d, split_tiles):
-    """The documented launch plan's workspace, restated: query tiles of 32 * 4 / heads-per-
+    """The documented launch plan's workspace (float32 rows, then float32 (m, l) pairs), restated: query tiles of 32 * 4 / heads-per-
     workgroup rows, key tiles of 64; runs only when split_tiles > 0, or automatically with
     at most 768 workgroups and fewer than 4 head slots (max(8, ceil(work / 256)) tiles)."""
     group = hq // hkv
@@ -221,7 +271,7 @@ def split_plan_bytes(m, hq, hkv, d, split_tiles):
     qt0 = next(qt for qt in range(nq) if nt[qt] > tiles)
     prow = (nq - qt0) * jmax * rows * hq
     up = lambda b: (b + 255) // 256 * 256
-    return up(prow * d * 2) + up(prow * 2 * 4)
+    return up(prow * d * 4) + up(prow * 2 * 4)
 
 
 def test_attention_split_plan_and_validation(lib):
@@ -230,8 +280,8 @@ def test_attention_split_plan_and_validation(lib):
     assert wsb(1088, 16, 8, 128, 0) == 0
     assert wsb(8256, 16, 8, 128, 0) == 0            # 128k: neither
     # runs of 3 key tiles forced: 6 runs at most, query tiles 3.. split:
-    # (17 - 3) * 6 * 64 rows * 16 heads of 128 halves + 2 floats
-    assert wsb(1088, 16, 8, 128, 3) == 86016 * 128 * 2 + 86016 * 2 * 4 == split_plan_bytes(1088, 16, 8, 128, 3)
+    # (17 - 3) * 6 * 64 rows * 16 heads of 128 floats + 2 floats
+    assert wsb(1088, 16, 8, 128, 3) == 86016 * 128 * 4 + 86016 * 2 * 4 == split_plan_bytes(1088, 16, 8, 128, 3)
     # one K/V head and its two query heads at 128k (the head-parallel shard): runs of 33 tiles
     assert wsb(8256, 2, 1, 128, 0) == split_plan_bytes(8256, 2, 1, 128, 0) > 0
     assert wsb(1088, 16, 8, 128, -1) == 0

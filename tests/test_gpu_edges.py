@@ -52,7 +52,7 @@ def test_select_edge_cases(case):
     for k in ks:
         log(f"[select {name}] n={len(s)} doc=[{b},{e}) k={k}")
         kept = binding.tg_select_topk(s32, b, e, k)
-        torch.cuda.synchronize()
+        binding.tg_select_check(binding.select_workspace(len(s), "cuda"))
         assert np.array_equal(kept.cpu().numpy().astype(np.int64), oracle.select_topk(s_exact, b, e, k))
 
 
@@ -64,19 +64,34 @@ def test_select_workspace_reuse_across_sizes():
     for n, q in ((200000, 16), (3000, 16), (77, 16), (150000, 1), (3000, 16), (140000, 64), (32768, 4)):
         s = np.round(g.normal(size=n) * q) / q
         k = int(g.integers(1, n - 10))
-        kept = binding.tg_select_topk(torch.from_numpy(s.astype(np.float32)).cuda(), 5, n - 5, k, workspace=ws)
+        st = torch.from_numpy(s.astype(np.float32)).cuda()
+        kept = binding.tg_select_topk(st, 5, n - 5, k, workspace=ws)
         assert np.array_equal(kept.cpu().numpy().astype(np.int64), oracle.select_topk(s, 5, n - 5, k))
-    torch.cuda.synchronize()
-    # barrier counters (bytes 0..7) and the digit histograms (2048 bins shared, then 2048 and
-    # 1024 bins for each of up to 8 budgets) are back at zero; the barrier-timeout flag
-    # (bytes 8..11) was never raised
-    assert int(ws[:12].count_nonzero()) == 0
-    assert int(ws[64:64 + 4 * (2048 + 8 * 2048 + 8 * 1024)].count_nonzero()) == 0
+        ks = [k, max(1, k // 3)]
+        for kk, lst in zip(ks, binding.tg_select_topk_multi(st, 5, n - 5, ks, workspace=ws)):
+            assert np.array_equal(lst.cpu().numpy().astype(np.int64), oracle.select_topk(s, 5, n - 5, kk))
+    binding.tg_select_check(ws)
+    assert_workspace_clean(ws)
+
+
+def assert_workspace_clean(ws):
+    """The parts of a selection workspace that must start at zero are zero again: the head
+    (barrier and exit counters, failure word, spin bound, candidate count: bytes 0..19), the
+    several-budget kernel's digit histograms (bytes 64 .. 106560: 2048 bins shared, then
+    2048 and 1024 bins for each of up to 8 budgets), the one-budget kernel's coarse, fine and
+    two digit histograms (bytes 110848 .. 179456: 256 + 16384 + 512 + 512 bins) and the ready
+    flags of its 64 chunks (the first word of each 128-byte line from byte 179456)."""
+    assert int(ws[:20].count_nonzero()) == 0
+    assert int(ws[64:106560].count_nonzero()) == 0
+    assert int(ws[110848:179456].count_nonzero()) == 0
+    ready = ws[179456:179456 + 64 * 128].view(64, 128)[:, :4]
+    assert int(ready.count_nonzero()) == 0
 
 
 # --------------------------------------------------------------------------- scorer
 @pytest.mark.parametrize("n,d_model,d_hidden,ldx", [
     (1, 64, 64, 64), (255, 128, 128, 128), (257, 256, 256, 320), (1000, 2048, 256, 2048), (3001, 512, 64, 576),
+    (777, 256, 192, 256), (1000, 2048, 192, 2112),
 ])
 def test_score_bf16_shapes(n, d_model, d_hidden, ldx):
     binding = require_gpu()

@@ -1,0 +1,153 @@
+"""tg_select_gather (the selection and the gather of the kept rows in one launch) and the
+selection's failure reporting, on the GPU against the float64 oracle.
+
+The top-K selector keeps the best document tokens and never prunes the question; layers
+above the gate see only the kept rows (aiproducthub.cn, section 事件详情; aisight.pl,
+section "Jak to dziala").  The kept positions must match the oracle's selection bit for
+bit, and the gathered rows and scores must be exact copies (compared as bit patterns, so
+-0, NaN and inf scores are checked too)."""
+import numpy as np
+import pytest
+
+import oracle
+from learned_token_pruning_scorer_amd import configs, inputs
+from gpu_common import gate_inputs, log, require_gpu
+from test_gpu_edges import _select_cases, assert_workspace_clean
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits32(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _check(binding, s_np, x_np, b, e, k, kept, xk, sk):
+    """kept vs the oracle, x_kept / s_kept vs host indexing, all bit-exact."""
+    s_exact = s_np.astype(np.float32).astype(np.float64)
+    ref = oracle.select_topk(s_exact, b, e, k)
+    got = kept.cpu().numpy().astype(np.int64)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(binding.to_host_bits(xk), x_np[ref])
+    assert np.array_equal(_bits32(sk.cpu().numpy()), _bits32(s_np.astype(np.float32))[ref])
+
+
+@pytest.mark.parametrize("case", _select_cases(), ids=lambda c: c[0])
+def test_select_gather_edge_cases(case):
+    """The selection edge cases (ties, +-0, NaN, inf, empty / middle / whole document,
+    ragged sizes, the heavy-tie path, more positions than the registers hold), each budget,
+    with a 64-wide bf16 row per position gathered."""
+    binding = require_gpu()
+    import torch
+    name, s, b, e, ks = case
+    n = len(s)
+    x_np = inputs.f32_to_bf16_bits(np.random.default_rng(n).normal(size=(n, 64)).astype(np.float32))
+    xt = binding.to_device(x_np, "bf16")
+    s32 = torch.from_numpy(s.astype(np.float32)).cuda()
+    ws = torch.zeros(binding.tg_select_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    for k in ks:
+        log(f"[select+gather {name}] n={n} doc=[{b},{e}) k={k}")
+        kept, xk, sk = binding.tg_select_gather(s32, xt, b, e, k, workspace=ws)
+        binding.tg_select_check(ws)
+        _check(binding, s, x_np, b, e, k, kept, xk, sk)
+    assert_workspace_clean(ws)
+
+
+@pytest.mark.parametrize("dtype,d_model,ldx,ld_out", [
+    ("bf16", 2048, 2048, 2048),   # 16-byte pieces, the workloads' rows
+    ("bf16", 10, 10, 10),         # 4-byte pieces
+    ("bf16", 7, 9, 11),           # 2-byte pieces, strided input and output
+    ("f32", 5, 6, 5),             # 4-byte pieces
+    ("f32", 256, 260, 256),       # 16-byte pieces, strided input
+])
+def test_select_gather_row_widths(dtype, d_model, ldx, ld_out):
+    binding = require_gpu()
+    import torch
+    g = np.random.default_rng(d_model * 7 + ldx)
+    n, b, e, k = 5000, 0, 4900, 700
+    s = g.normal(size=n)
+    xf = g.normal(size=(n, ldx)).astype(np.float32)
+    x_np = inputs.f32_to_bf16_bits(xf) if dtype == "bf16" else xf
+    xt = binding.to_device(x_np, dtype)[:, :d_model]
+    out = torch.zeros(tg_m := binding.tg_num_kept(n, b, e, k), ld_out, dtype=xt.dtype, device="cuda")[:, :d_model]
+    log(f"[select+gather widths] {dtype} d_model={d_model} ldx={ldx} ld_out={ld_out}")
+    kept, xk, sk = binding.tg_select_gather(torch.from_numpy(s.astype(np.float32)).cuda(), xt, b, e, k, x_kept=out)
+    _check(binding, s, x_np[:, :d_model], b, e, k, kept, xk, sk)
+    assert xk.shape == (tg_m, d_model)
+
+
+@pytest.mark.parametrize("name", ["niah16k", "mdqa32k", "long128k"])
+def test_select_gather_matches_select_then_gather(name):
+    """On the workloads' own scores and hidden states: the fused call gives exactly what
+    tg_select_topk followed by tg_gather_kept gives, and the oracle's selection."""
+    binding = require_gpu()
+    import torch
+    w = configs.WORKLOADS[name]
+    gi = gate_inputs(name)
+    k = w.budgets[0]
+    x = binding.to_device(gi.x, w.dtype)
+    s = binding.tg_gate_score(x, binding.to_device(gi.w1, w.dtype), binding.to_device(gi.w2, w.dtype),
+                              torch.from_numpy(gi.b1).cuda(), gi.b2)
+    log(f"[select+gather {name}] n={w.n} k={k}")
+    kept, xk, sk = binding.tg_select_gather(s, x, w.doc_begin, w.doc_end, k)
+    kept2 = binding.tg_select_topk(s, w.doc_begin, w.doc_end, k)
+    xk2, sk2 = binding.tg_gather_kept(x, kept2, s)
+    torch.cuda.synchronize()
+    assert torch.equal(kept, kept2)
+    assert torch.equal(xk.view(torch.int16), xk2.view(torch.int16))
+    assert torch.equal(sk.view(torch.int32), sk2.view(torch.int32))
+    s_np = s.cpu().numpy()
+    assert np.array_equal(kept.cpu().numpy().astype(np.int64),
+                          oracle.select_topk(s_np.astype(np.float64), w.doc_begin, w.doc_end, k))
+    assert np.array_equal(binding.to_host_bits(xk), gi.x[kept.cpu().numpy()])
+
+
+def test_given_up_wait_is_reported_and_sticky():
+    """Forced from the host: the workspace's spin-bound word set to 0xFFFFFFFF makes every
+    wait give up at once (every kernel still exits normally).  tg_select_check then raises,
+    later selections on that workspace write nothing, and a zero-fill restores it."""
+    binding = require_gpu()
+    import torch
+    g = np.random.default_rng(11)
+    n, b, e, k = 100000, 0, 99000, 5000
+    s_np = g.normal(size=n)
+    st = torch.from_numpy(s_np.astype(np.float32)).cuda()
+    x_np = inputs.f32_to_bf16_bits(g.normal(size=(n, 64)).astype(np.float32))
+    xt = binding.to_device(x_np, "bf16")
+    m = binding.tg_num_kept(n, b, e, k)
+    ws = torch.zeros(binding.tg_select_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    ws[12:16] = 0xFF
+    kept = torch.full((m,), -1, dtype=torch.int32, device="cuda")
+    binding.tg_select_gather(st, xt, b, e, k, kept=kept, workspace=ws)
+    with pytest.raises(binding.TokenGateError) as err:
+        binding.tg_select_check(ws)
+    assert err.value.status == 5
+    ws[12:16] = 0   # the bound is back to normal, but the failure word stays set
+    binding.tg_select_topk(st, b, e, k, out=kept, workspace=ws)
+    binding.tg_select_topk_multi(st, b, e, [k, 7], workspace=ws)
+    with pytest.raises(binding.TokenGateError):
+        binding.tg_select_check(ws)
+    assert int((kept != -1).sum()) == 0   # nothing was written
+    ws.zero_()
+    kept2, xk, sk = binding.tg_select_gather(st, xt, b, e, k, workspace=ws)
+    binding.tg_select_check(ws)
+    _check(binding, s_np, x_np, b, e, k, kept2, xk, sk)
+    # the several-budget kernel honours the same word
+    ws[12:16] = 0xFF
+    binding.tg_select_topk_multi(st, b, e, [k, 7], workspace=ws)
+    with pytest.raises(binding.TokenGateError):
+        binding.tg_select_check(ws)
+
+
+def test_workspace_not_zero_filled_is_reported():
+    """A workspace whose histogram is not zero (never zero-filled) is detected: the coarse
+    histogram's total differs from the document length, and the call reports failure
+    instead of selecting from a corrupt histogram."""
+    binding = require_gpu()
+    import torch
+    n, b, e, k = 50000, 0, 49000, 3000
+    st = torch.from_numpy(np.random.default_rng(12).normal(size=n).astype(np.float32)).cuda()
+    ws = torch.zeros(binding.tg_select_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    ws[110848:110848 + 1024] = 1   # the coarse histogram's bytes
+    binding.tg_select_topk(st, b, e, k, workspace=ws)
+    with pytest.raises(binding.TokenGateError):
+        binding.tg_select_check(ws)

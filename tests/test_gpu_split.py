@@ -6,7 +6,7 @@ section 事件详情; aisight.pl, section "Jak to dziala"), with each long query
 walked by two groups of waves, or cut into runs over workgroups, whose partial softmax
 states are merged.  Its output is judged with the
 attention tolerances (bf16: max-abs 2e-2, mean-abs 2e-3); the runs' normalised rows are
-kept in float16 (2^-11 relative, far inside them).  The lse merge adds only float32
+kept in float32.  The lse merge adds only float32
 rounding to the unsplit kernel's arithmetic, so the lse is held to the backward
 test's 2e-2 and, against the unsplit kernel's own lse, to 2^-7: each side's row sum adds
 P values rounded to bf16 (unit roundoff 2^-8) against its own running max, so each log

@@ -326,6 +326,8 @@ def test_splitmix64_known_answers(golden_dir):
     rows = [l for l in open(os.path.join(golden_dir, "splitmix64_seed1234567.txt")) if not l.startswith("#")]
     expect = np.array([int(l) for l in rows], dtype=np.uint64)
     assert np.array_equal(oracle.splitmix64(1234567, len(expect)), expect)
+    # the random selector's key of position i is the HIGH half of output i (not the low one)
+    assert np.array_equal(oracle.random_keys(1234567, len(expect)), (expect >> np.uint64(32)).astype(np.uint32))
 
 
 def test_random_keys_are_uniform_and_independent():
