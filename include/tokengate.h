@@ -155,6 +155,26 @@ tg_status tg_select_gather(int32_t dtype, int64_t n, int32_t d_model, const floa
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * tg_select_gather_noalloc -- tg_select_gather without a workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, serving loops that
+ * must not call hipMalloc, harnesses that forbid allocation.  The workspace is a static
+ * device array of tg_select_workspace_bytes' fixed size (217 KiB, enough for every n: the
+ * selection's layout does not depend on n), one per device, held by the library until the
+ * process ends.  Each call clears it on `stream` with a small fill kernel before selecting,
+ * so a call that gave up leaves nothing behind for the next.  Calls that overlap on one
+ * device (two streams, or two host threads) share that array and race: serialise them.
+ * Calls no hipMalloc, hipFree or other allocating routine.
+ *   status  NULL, or one device int32 that the call sets to 0 on the stream and to 1 if a
+ *           wait of the selection gave up (its outputs are then invalid); not touched when
+ *           nothing is kept (m = 0)
+ * Other arguments, outputs and errors as tg_select_gather.
+ */
+tg_status tg_select_gather_noalloc(int32_t dtype, int64_t n, int32_t d_model, const float* scores,
+                                   int64_t doc_begin, int64_t doc_end, int64_t k, const void* x, int64_t ldx,
+                                   int32_t* kept_idx, void* x_kept, int64_t ld_out, float* s_kept,
+                                   int32_t* status, void* stream);
+
+/*
  * tg_select_check -- whether every selection enqueued so far on `workspace` completed.
  * Synchronises `stream` (the host blocks until the stream's work is done), then reads
  * the workspace's sticky failure word: TG_OK if it is clear; TG_ERR_INCOMPLETE if a

@@ -54,6 +54,8 @@ _lib.tg_select_topk_multi.restype = _i32
 _lib.tg_select_topk_multi.argtypes = [_i64, _p, _i64, _i64, ctypes.POINTER(ctypes.c_int64), _i32, _p, _p, _sz, _p]
 _lib.tg_select_gather.restype = _i32
 _lib.tg_select_gather.argtypes = [_i32, _i64, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _sz, _p]
+_lib.tg_select_gather_noalloc.restype = _i32
+_lib.tg_select_gather_noalloc.argtypes = [_i32, _i64, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _p, _p]
 _lib.tg_select_check.restype = _i32
 _lib.tg_select_check.argtypes = [_p, _sz, _p]
 _lib.tg_check_positions.restype = _i32
@@ -251,6 +253,31 @@ def tg_select_gather(scores, x, doc_begin: int, doc_end: int, k: int, kept=None,
         _dtype_code(x), n, d_model, _ptr(scores), doc_begin, doc_end, k, _ptr(x), x.stride(0), _ptr(kept),
         _ptr(x_kept), x_kept.stride(0), _ptr(s_kept), _ptr(ws), ws.numel() * ws.element_size(),
         _stream(dev, stream)))
+    return kept[:m], x_kept[:m], s_kept[:m]
+
+
+def tg_select_gather_noalloc(scores, x, doc_begin: int, doc_end: int, k: int, kept, x_kept, s_kept, status=None,
+                             stream=None):
+    """tg_select_gather on the library's static device scratch (no workspace, nothing allocated
+    by the library): outputs kept [>= m] int32, x_kept [>= m, d_model], s_kept [>= m] float32
+    and the optional status (one int32: 1 if a wait gave up) are the caller's."""
+    dev = _on_gpu(scores, x, kept, x_kept, s_kept, status)
+    n, d_model = x.shape
+    m = tg_num_kept(n, doc_begin, doc_end, k)
+    if m < 0:
+        raise ValueError("invalid document span or budget")
+    if scores.dtype != torch.float32 or scores.shape != (n,) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 vector with one entry per row of x")
+    if x.stride(1) != 1 or x_kept.dtype != x.dtype or x_kept.shape[0] < m or x_kept.shape[1] != d_model \
+            or x_kept.stride(1) != 1:
+        raise ValueError("x and x_kept must be [rows, d_model] of one dtype with unit column stride")
+    if kept.dtype != torch.int32 or kept.numel() < m or s_kept.dtype != torch.float32 or s_kept.numel() < m:
+        raise ValueError("kept (int32) and s_kept (float32) need room for m entries")
+    if status is not None and (status.dtype != torch.int32 or status.numel() < 1):
+        raise ValueError("status must be an int32 tensor of at least one element")
+    _check("tg_select_gather_noalloc", _lib.tg_select_gather_noalloc(
+        _dtype_code(x), n, d_model, _ptr(scores), doc_begin, doc_end, k, _ptr(x), x.stride(0), _ptr(kept),
+        _ptr(x_kept), x_kept.stride(0), _ptr(s_kept), _ptr(status), _stream(dev, stream)))
     return kept[:m], x_kept[:m], s_kept[:m]
 
 

@@ -58,6 +58,7 @@
 // uniformly random K-subset of the document.
 #include <atomic>
 #include <cstddef>
+#include <mutex>
 
 #include "tg_common.h"
 
@@ -458,6 +459,7 @@ struct SgArgs {
   int chunk;             // positions per selection workgroup (a multiple of kSgThreads)
   int nsel;              // selection workgroups (chunks); the grid is nsel x team
   int vec;               // scores 16-byte aligned: 8 consecutive positions load as two vectors
+  uint32_t* status;      // NULL, or a word set to 1 when a wait gives up (allocation-free calls)
   int m;                 // kept positions
   char* ws;
   int32_t* kept;
@@ -468,6 +470,15 @@ struct SgArgs {
   int row_b;             // bytes copied per row
   int unit;              // copy unit in bytes: 16, 4 or 2
 };
+
+// Clears `words` words at p, and *status if given (the allocation-free entry point's
+// scratch and its caller's status word).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, uint32_t words,
+                                                         uint32_t* __restrict__ status) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i < words) p[i] = 0u;
+  if (status && i == 0) *status = 0u;
+}
 
 template <typename U>
 __device__ __forceinline__ void copy_rows(const SgArgs& a, const int32_t* lrow, int64_t s0, int nrows) {
@@ -523,7 +534,14 @@ __global__ __launch_bounds__(kSgThreads, 2) void sel_gather_kernel(SgArgs a) {
   const int w = blockIdx.x % G;            // this workgroup's chunk
   const int share = blockIdx.x / G;        // 0: selects chunk w and copies the first share of its rows
   const int team = gridDim.x / G;          // workgroups copying chunk w's rows (1 without the gather)
-  if (!workspace_ok(st, &sh_flag)) return;   // an earlier call on this workspace gave up
+  // a wait that gives up also marks the caller's status word, if there is one
+  auto fail_out = [&a]() {
+    if (threadIdx.x == 0 && a.status) st_agent(a.status, 1u);
+  };
+  if (!workspace_ok(st, &sh_flag)) {   // an earlier call on this workspace gave up
+    fail_out();
+    return;
+  }
   const uint32_t limit = spin_bound(st);
   uint32_t* flag_line = gteam + w * kSgTeamWords;   // [0] ready, [1] first slot, [2] slots
 
@@ -603,7 +621,10 @@ __global__ __launch_bounds__(kSgThreads, 2) void sel_gather_kernel(SgArgs a) {
         const uint32_t v = lbuf[f];
         if (v) atomicAdd(&gfine[f], v);
       }
-      if (!grid_barrier(st, ++nbar * G, limit, &sh_flag)) return;
+      if (!grid_barrier(st, ++nbar * G, limit, &sh_flag)) {
+        fail_out();
+        return;
+      }
 
       // ---- 2. the fine bin holding the k_eff-th largest key, and the rank inside it ----
       uint32_t rank = a.k_eff;   // 0 < k_eff < D
@@ -613,6 +634,7 @@ __global__ __launch_bounds__(kSgThreads, 2) void sel_gather_kernel(SgArgs a) {
         const uint32_t above = block_excl_scan_n<NT>(cv, &tot, sh);
         if (tot != (uint32_t)(a.doc_end - a.doc_begin)) {   // the workspace was not zero: give up
           if (tid == 0) atomicOr(&st->fail, 1u);
+          fail_out();
           return;
         }
         if (above < rank && rank <= above + cv) {
@@ -672,7 +694,10 @@ __global__ __launch_bounds__(kSgThreads, 2) void sel_gather_kernel(SgArgs a) {
           }
         });
       }
-      if (!grid_barrier(st, ++nbar * G, limit, &sh_flag)) return;
+      if (!grid_barrier(st, ++nbar * G, limit, &sh_flag)) {
+        fail_out();
+        return;
+      }
       // every selection workgroup has read the histograms: clear them for the next call
       for (int i = w * (kSgFine / G) + tid; i < (w + 1) * (kSgFine / G); i += NT) st_agent(&gfine[i], 0u);
       if (w == G - 1)
@@ -762,7 +787,10 @@ __global__ __launch_bounds__(kSgThreads, 2) void sel_gather_kernel(SgArgs a) {
           __syncthreads();
           if (lh[tid]) atomicAdd(&gd[tid], lh[tid]);
           if (lh[tid + NT]) atomicAdd(&gd[tid + NT], lh[tid + NT]);
-          if (!grid_barrier(st, ++nbar * G, limit, &sh_flag)) return;
+          if (!grid_barrier(st, ++nbar * G, limit, &sh_flag)) {
+        fail_out();
+        return;
+      }
           if (pass == 1 && w == 0) {   // digit a was read by everyone before this barrier
             st_agent(&gda[tid], 0u);
             st_agent(&gda[tid + NT], 0u);
@@ -798,7 +826,10 @@ __global__ __launch_bounds__(kSgThreads, 2) void sel_gather_kernel(SgArgs a) {
           st_agent(&ggt[w], ngt);
           st_agent(&geq[w], neq);
         }
-        if (!grid_barrier(st, ++nbar * G, limit, &sh_flag)) return;
+        if (!grid_barrier(st, ++nbar * G, limit, &sh_flag)) {
+        fail_out();
+        return;
+      }
         if (w == 0) {   // digit b was read by everyone before this barrier
           st_agent(&gdb[tid], 0u);
           st_agent(&gdb[tid + NT], 0u);
@@ -917,7 +948,10 @@ __global__ __launch_bounds__(kSgThreads, 2) void sel_gather_kernel(SgArgs a) {
       sh_flag = ok;
     }
     __syncthreads();
-    if (!sh_flag) return;
+    if (!sh_flag) {
+      fail_out();
+      return;
+    }
   }
 
   // ---- 5. the gather: this workgroup's share of chunk w's slots ----
@@ -1030,10 +1064,16 @@ static tg_status launch_select(int64_t n, const SelKeys& src, int64_t doc_begin,
 }
 
 // One budget, with the gather of the kept rows when x is given (sel_gather_kernel).
+static void* scratch_address(int device);
+
+// use_scratch: the allocation-free variant: the workspace is this device's static scratch
+// array, cleared on the stream before the selection (its contents are whatever the last
+// call left, which may have given up).
 static tg_status launch_select_gather(int64_t n, const float* scores, int64_t doc_begin, int64_t doc_end, int64_t k,
                                       int32_t* kept_idx, float* s_kept, int32_t dtype, int32_t d_model, const void* x,
                                       int64_t ldx, void* x_kept, int64_t ld_out, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+                                      size_t workspace_bytes, void* stream, bool use_scratch = false,
+                                      uint32_t* status = nullptr) {
   if (n <= 0 || n > INT32_MAX || k < 0) return TG_ERR_INVALID_ARG;
   const int64_t m = tg_num_kept(n, doc_begin, doc_end, k);
   if (m < 0) return TG_ERR_INVALID_ARG;
@@ -1053,11 +1093,15 @@ static tg_status launch_select_gather(int64_t n, const float* scores, int64_t do
     a.unit = (align & 15u) == 0 ? 16 : ((align & 3u) == 0 ? 4 : 2);
   }
   if (m == 0) return TG_OK;   // nothing kept, nothing to write
-  if (!scores || !kept_idx || !workspace) return TG_ERR_INVALID_ARG;
+  if (!scores || !kept_idx || (!workspace && !use_scratch)) return TG_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return TG_ERR_INVALID_ARG;
-  if (workspace_bytes < SgLayout::bytes) return TG_ERR_WORKSPACE;
+  if (!use_scratch && workspace_bytes < SgLayout::bytes) return TG_ERR_WORKSPACE;
   int device = 0;
   if (hipGetDevice(&device) != hipSuccess) return TG_ERR_HIP;
+  if (use_scratch) {
+    workspace = scratch_address(device);
+    if (!workspace) return TG_ERR_HIP;
+  }
   const int cap = coresident_blocks<1>(device, reinterpret_cast<const void*>(sel_gather_kernel), kSgThreads);
   if (cap <= 0) return TG_ERR_HIP;
   int64_t nsel = (n + kSgThreads - 1) / kSgThreads;
@@ -1091,13 +1135,40 @@ static tg_status launch_select_gather(int64_t n, const float* scores, int64_t do
   a.ws = static_cast<char*>(workspace);
   a.kept = kept_idx;
   a.s_kept = s_kept;
+  a.status = status;
+  if (use_scratch) {
+    const uint32_t words = static_cast<uint32_t>(SgLayout::bytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint32_t*>(workspace), words, status);
+    TG_CHECK_LAUNCH();
+  }
   hipLaunchKernelGGL(sel_gather_kernel, dim3(static_cast<unsigned>(grid)), dim3(kSgThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   TG_CHECK_LAUNCH();
   return TG_OK;
 }
 
+// ---------------------------------------------------------------------------------
+// Allocation-free selection + gather: the workspace is a static device array, one per
+// device, held by the library until the process ends.
+// ---------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = SgLayout::bytes;   // 217 KiB: the selection's layout does not depend on n
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
+// Device address of `scratch` on `device` (the current device), looked up once per device
+// with that device current; NULL if the runtime cannot give it.
+static void* scratch_address(int device) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  if (device < 0 || device >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[device] = p;
+  }
+  return addr[device];
+}
 
 }  // namespace tg
 
@@ -1115,6 +1186,17 @@ extern "C" tg_status tg_select_gather(int32_t dtype, int64_t n, int32_t d_model,
   if (!x || !s_kept) return TG_ERR_INVALID_ARG;
   return tg::launch_select_gather(n, scores, doc_begin, doc_end, k, kept_idx, s_kept, dtype, d_model, x, ldx, x_kept,
                                   ld_out, workspace, workspace_bytes, stream);
+}
+
+extern "C" tg_status tg_select_gather_noalloc(int32_t dtype, int64_t n, int32_t d_model, const float* scores,
+                                              int64_t doc_begin, int64_t doc_end, int64_t k, const void* x,
+                                              int64_t ldx, int32_t* kept_idx, void* x_kept, int64_t ld_out,
+                                              float* s_kept, int32_t* status, void* stream) {
+  if (!x || !s_kept) return TG_ERR_INVALID_ARG;
+  // the scratch array has the selection's fixed layout, whatever n is: never exceeded
+  if (tg_select_workspace_bytes(n) > tg::kScratchBytes) return TG_ERR_WORKSPACE;
+  return tg::launch_select_gather(n, scores, doc_begin, doc_end, k, kept_idx, s_kept, dtype, d_model, x, ldx, x_kept,
+                                  ld_out, nullptr, 0, stream, true, reinterpret_cast<uint32_t*>(status));
 }
 
 extern "C" tg_status tg_select_check(const void* workspace, size_t workspace_bytes, void* stream) {

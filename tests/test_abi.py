@@ -147,6 +147,25 @@ def test_select_gather_validation(lib):
     assert call(e=1000, k=0, s=None, kept=None, ws=None, need=0) == TG_OK
 
 
+def test_select_gather_noalloc_validation(lib):
+    i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.tg_select_gather_noalloc.argtypes = [i32, i64, i32, p, i64, i64, i64, p, i64, p, p, i64, p, p, p]
+
+    def call(**kw):
+        a = dict(dtype=1, n=1000, d=64, s=FAKE, b=0, e=900, k=10, x=FAKE, ldx=64, kept=FAKE, xk=FAKE, ldo=64, sk=FAKE)
+        a.update(kw)
+        return lib.tg_select_gather_noalloc(a["dtype"], a["n"], a["d"], a["s"], a["b"], a["e"], a["k"], a["x"],
+                                            a["ldx"], a["kept"], a["xk"], a["ldo"], a["sk"], None, None)
+    assert call(x=None) == TG_ERR_INVALID_ARG
+    assert call(sk=None) == TG_ERR_INVALID_ARG
+    assert call(s=None) == TG_ERR_INVALID_ARG
+    assert call(kept=None) == TG_ERR_INVALID_ARG
+    assert call(ldx=32) == TG_ERR_INVALID_ARG
+    assert call(k=-1) == TG_ERR_INVALID_ARG
+    assert call(n=0) == TG_ERR_INVALID_ARG
+    assert call(e=1000, k=0, s=None, kept=None) == TG_OK   # nothing kept: a no-op
+
+
 def test_select_check_validation(lib):
     assert lib.tg_select_check(None, 1 << 20, None) == TG_ERR_INVALID_ARG
     assert lib.tg_select_check(FAKE, 8, None) == TG_ERR_INVALID_ARG
