@@ -2,10 +2,9 @@
 """Throughput of the TokenGate gated-prefill hot path on one MI355X.
 
 One step = the whole path over one prompt already resident in HBM:
-    tg_gate_score (N rows) -> tg_select_gather (top-K select + gather of the kept rows,
-    one launch) -> tg_gated_attention_split (M rows)
+    tg_gate_score (N rows) -> tg_select_topk -> tg_gather_kept -> tg_gated_attention_split (M rows)
 (the gated attention with the library's own launch plan: at long contexts it is the plain
-tg_gated_attention kernel).  The three launches of a step are captured once in a HIP graph
+tg_gated_attention kernel).  The four launches of a step are captured once in a HIP graph
 (torch.cuda.CUDAGraph over the library's calls) and replayed: `value` = prompt tokens per
 second = N / (wall time of one step), K replays timed back-to-back between two device
 synchronisations (warm caches: nothing is flushed between replays; `cold_ms_per_step` is
@@ -39,7 +38,7 @@ METRIC = "gated-prefill input tokens/s at 16k/128k; attn TFLOP/s and select GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 CALIB_BYTES = 1 << 30          # streaming copy in --profile-steps mode: reads and writes this many bytes
-STAGES = ("score", "select_gather", "attention")   # the step's launches, in order
+STAGES = ("score", "select", "gather", "attention")   # the step's launches, in order
 # HBM bytes per launch of the attention kernel on long128k, from rocprofv3 FETCH_SIZE and WRITE_SIZE
 # scaled by the same counters' reading of the calibration copy (profiles/long128k_hbm_counters.md).
 # Reported only while the kernel source is the one the counters were taken on.
@@ -137,11 +136,12 @@ class Path:
         if ev: ev[0].record()
         b.tg_gate_score(self.x, self.w1, self.w2, self.b1, self.gi.b2, out=self.scores)
         if ev: ev[1].record()
-        b.tg_select_gather(self.scores, self.x, w.doc_begin, w.doc_end, self.k, kept=self.kept, x_kept=self.xk,
-                           s_kept=self.sk, workspace=self.ws)
+        b.tg_select_topk(self.scores, w.doc_begin, w.doc_end, self.k, out=self.kept, workspace=self.ws)
         if ev: ev[2].record()
-        self.attention()
+        b.tg_gather_kept(self.x, self.kept, self.scores, out=self.xk, s_out=self.sk)
         if ev: ev[3].record()
+        self.attention()
+        if ev: ev[4].record()
 
     def graph(self):
         """The step captured in a HIP graph (after warm-up launches on a side stream)."""
@@ -258,17 +258,14 @@ def next_rows(path, reps):
     us_fwd = _event_time_us(torch, lambda: b.tg_gated_attention_lse(
         path.q, path.kk, path.v, path.kept, path.sk, path.gain, path.tau, out=out, lse=lse), reps)
     res["attention_forward_with_lse"] = {"us": us_fwd}
-    # the same selection and gather as two launches (tg_select_topk, then tg_gather_kept)
+    # the same selection and gather in one launch (tg_select_gather, the allocation-free path's kernel)
     kept2 = torch.empty_like(path.kept)
     xk2, sk2 = torch.empty_like(path.xk), torch.empty_like(path.sk)
-
-    def two_calls():
-        b.tg_select_topk(path.scores, w.doc_begin, w.doc_end, path.k, out=kept2, workspace=path.ws)
-        b.tg_gather_kept(path.x, kept2, path.scores, out=xk2, s_out=sk2)
-    us = _event_time_us(torch, two_calls, reps)
+    us = _event_time_us(torch, lambda: b.tg_select_gather(path.scores, path.x, w.doc_begin, w.doc_end, path.k,
+                                                          kept=kept2, x_kept=xk2, s_kept=sk2, workspace=path.ws), reps)
     byts = algorithmic(w, path.k)["select_gather_bytes"]
-    res["select_then_gather"] = {"us": us, "frac_hbm_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                                 "note": "tg_select_topk then tg_gather_kept (two launches) on the step's inputs"}
+    res["select_gather_one_launch"] = {"us": us, "frac_hbm_peak": byts / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                                       "note": "tg_select_gather (selection and row gather fused) on the step's inputs"}
     del kept2, xk2, sk2
     # several budgets over one histogram of the same scores
     ks = [path.k // 8, path.k // 4, path.k // 2, path.k]
@@ -493,13 +490,13 @@ def main():
     sec_cold = path.timed_cold(max(5, args.steps // 2))
     w = path.w
     alg = algorithmic(w, path.k)
-    attn_tflops = alg["attn_flops"] / (stage_mean[2] * 1e-6) / 1e12
-    sel_gather_gbs = alg["select_gather_bytes"] / (stage_mean[1] * 1e-6) / 1e9
+    attn_tflops = alg["attn_flops"] / (stage_mean[3] * 1e-6) / 1e12
+    sel_gather_gbs = alg["select_gather_bytes"] / ((stage_mean[1] + stage_mean[2]) * 1e-6) / 1e9
     score_gbs = alg["score_bytes"] / (stage_mean[0] * 1e-6) / 1e9
     score_tflops = alg["score_flops"] / (stage_mean[0] * 1e-6) / 1e12
     print(f"[bench] {args.workload}: {sec * 1e3:.3f} ms/step (graph), {sec_eager * 1e3:.3f} eager; "
-          f"stages us (mean) score {stage_mean[0]:.1f} select+gather {stage_mean[1]:.1f} "
-          f"attention {stage_mean[2]:.1f}", file=sys.stderr, flush=True)
+          f"stages us (mean) score {stage_mean[0]:.1f} select {stage_mean[1]:.1f} gather {stage_mean[2]:.1f} "
+          f"attention {stage_mean[3]:.1f}", file=sys.stderr, flush=True)
 
     also = []
     for name in [a for a in args.also.split(",") if a and a != args.workload]:
@@ -514,8 +511,9 @@ def main():
                      "eager_ms_per_step": sec2e * 1e3, "eager_tokens_per_s": p2.w.n / sec2e,
                      "stage_us_mean": dict(zip(STAGES, (float(v) for v in st2))),
                      "stage_us_median": dict(zip(STAGES, (float(v) for v in st2m))),
-                     "attention_frac_mfma_peak": alg2["attn_flops"] / (st2[2] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
-                     "select_gather_frac_hbm_peak": alg2["select_gather_bytes"] / (st2[1] * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                     "attention_frac_mfma_peak": alg2["attn_flops"] / (st2[3] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+                     "select_gather_frac_hbm_peak":
+                         alg2["select_gather_bytes"] / ((st2[1] + st2[2]) * 1e-6) / 1e9 / PEAK_HBM_GBS,
                      "score_frac_hbm_peak": alg2["score_bytes"] / (st2[0] * 1e-6) / 1e9 / PEAK_HBM_GBS})
         print(f"[bench] {name}: {sec2 * 1e3:.3f} ms/step (graph)", file=sys.stderr, flush=True)
         del p2
@@ -546,7 +544,7 @@ def main():
         "ms_per_step": sec * 1e3,
         "eager_ms_per_step": sec_eager * 1e3,
         "cold_ms_per_step": sec_cold * 1e3,
-        "step_launch": "HIP graph of the step's three launches (score, select+gather, attention), replayed back "
+        "step_launch": "HIP graph of the step's four launches (score, select, gather, attention), replayed back "
                        "to back; eager steps give the stage times",
         "value_cache_state": "warm: back-to-back replays, nothing flushed between them (X of the 128k workload, "
                              "512 MiB, exceeds the 256 MB Infinity Cache anyway); cold_ms_per_step = median "

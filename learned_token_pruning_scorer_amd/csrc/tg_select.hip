@@ -177,18 +177,27 @@ __device__ __forceinline__ bool workspace_ok(SelState* st, uint32_t* flag) {
   return ok;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP row moves (no LDS round
+// trips): shifts of 1, 2, 4, 8 inside each row of 16 lanes, then the last lane of row r
+// is broadcast into row r + 1 (rows 1, 3) and lane 31 into rows 2, 3.  A lane whose DPP
+// source does not exist adds 0.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  return v;
+}
+
 // Exclusive scan of one value per thread over a workgroup of NT threads; *total gets
 // the sum.  sh: NT / 64 words of LDS.
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan_n(uint32_t v, uint32_t* total, uint32_t* sh) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) sh[wave] = incl;
   __syncthreads();
   uint32_t wbase = 0, tot = 0;
@@ -206,9 +215,8 @@ __device__ __forceinline__ uint32_t block_excl_scan_n(uint32_t v, uint32_t* tota
 template <int NT>
 __device__ __forceinline__ uint32_t block_sum_n(uint32_t v, uint32_t* sh) {
   constexpr int NW = NT / 64;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  v = wave_incl_scan(v);
+  if ((threadIdx.x & 63) == 63) sh[threadIdx.x >> 6] = v;
   __syncthreads();
   uint32_t tot = 0;
 #pragma unroll
@@ -229,7 +237,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(SelKeys src, int
                                                                 int32_t* __restrict__ kept) {
   __shared__ uint32_t lh[NKM * kSelMaxBins];
   __shared__ uint32_t sh[kSelWaves];
-  __shared__ uint32_t sh_prefix, sh_rank, sh_flag;
+  __shared__ uint32_t sh_prefix, sh_rank, sh_count, sh_flag;
   SelState* st = reinterpret_cast<SelState*>(ws + SelLayout::state);
   if (!workspace_ok(st, &sh_flag)) return;   // an earlier call on this workspace gave up
   const uint32_t limit = spin_bound(st);
@@ -267,11 +275,14 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(SelKeys src, int
 
   // per budget: digit prefix fixed so far and rank still to find; at the end, the
   // threshold key T and the number of keys equal to T that are kept
-  uint32_t prefix[NKM], rank[NKM];
+  // expect: the keys the next digit's histogram must hold (the document, then the
+  // chosen bin's count); a histogram that sums to anything else was not zero at the start
+  uint32_t prefix[NKM], rank[NKM], expect[NKM];
   bool any_select = false;
 #pragma unroll
   for (int b = 0; b < NKM; ++b) {
     prefix[b] = 0u;
+    expect[b] = static_cast<uint32_t>(doc_end - doc_begin);
     rank[b] = b < nk ? bud.k_eff[b] : 0u;
     any_select |= b < nk && bud.mode[b] == 2;
   }
@@ -323,6 +334,10 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(SelKeys src, int
         }
         uint32_t total;
         uint32_t above = block_excl_scan(local, &total, sh);
+        if (total != expect[b]) {   // same value in every workgroup: all of them give up
+          if (tid == 0) atomicOr(&st->fail, 1u);
+          return;
+        }
         if (above < rank[b] && rank[b] <= above + local) {
 #pragma unroll
           for (uint32_t q = 0; q < 4; ++q) {
@@ -330,6 +345,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(SelKeys src, int
               if (rank[b] <= above + c[q]) {
                 sh_prefix = (prefix[b] << bits) | (bins - 1 - (tid * per + q));
                 sh_rank = rank[b] - above;
+                sh_count = c[q];
                 break;
               }
               above += c[q];
@@ -339,6 +355,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_fused_kernel(SelKeys src, int
         __syncthreads();
         prefix[b] = sh_prefix;
         rank[b] = sh_rank;
+        expect[b] = sh_count;
         __syncthreads();   // sh_prefix / sh_rank are reused by the next budget
       }
     }
@@ -646,12 +663,7 @@ __global__ __launch_bounds__(kSgThreads, 2) void sel_gather_kernel(SgArgs a) {
         if (tid < 64) {   // one wave scans the 64 fine bins under cb from the top
           const uint32_t f = cb * kSgFinePerCoarse + (kSgFinePerCoarse - 1 - tid);
           const uint32_t fv = ld_agent(&gfine[f]);
-          uint32_t incl = fv;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(incl, o, 64);
-            if (tid >= o) incl += y;
-          }
+          const uint32_t incl = wave_incl_scan(fv);
           if (incl - fv < rc && rc <= incl) {
             bc[3] = f;
             bc[4] = rc - (incl - fv);
@@ -673,9 +685,16 @@ __global__ __launch_bounds__(kSgThreads, 2) void sel_gather_kernel(SgArgs a) {
         ns += (!doc || f > fb) ? 1u : 0u;
         nc += (doc && f == fb) ? 1u : 0u;
       });
-      ns = block_sum_n<NT>(ns, sh);
-      uint32_t nc_tot;
-      uint32_t slot = block_excl_scan_n<NT>(nc, &nc_tot, sh);
+      uint32_t slot, nc_tot;
+      if (a.chunk < 65536) {   // both counts in one scan (each is at most the chunk)
+        uint32_t both;
+        slot = block_excl_scan_n<NT>(ns | (nc << 16), &both, sh) >> 16;
+        ns = both & 0xffffu;
+        nc_tot = both >> 16;
+      } else {
+        ns = block_sum_n<NT>(ns, sh);
+        slot = block_excl_scan_n<NT>(nc, &nc_tot, sh);
+      }
       if (tid == 0) {
         st_agent(&gsure[w], ns);
         if (fits && nc_tot) bc[6] = atomicAdd(&st->ncand, nc_tot);
@@ -732,12 +751,7 @@ __global__ __launch_bounds__(kSgThreads, 2) void sel_gather_kernel(SgArgs a) {
               h[q] = lh[kSgDigit - 1 - 8 * lane - q];
               sum += h[q];
             }
-            uint32_t incl = sum;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-              const uint32_t y = __shfl_up(incl, o, 64);
-              if (lane >= o) incl += y;
-            }
+            const uint32_t incl = wave_incl_scan(sum);
             uint32_t ab = incl - sum, digit = 0u, r2 = 0u;
             const bool here = ab < rk && rk <= incl;
             if (here) {
@@ -1175,8 +1189,9 @@ static void* scratch_address(int device) {
 extern "C" tg_status tg_select_topk(int64_t n, const float* scores, int64_t doc_begin, int64_t doc_end,
                                     int64_t k, int32_t* kept_idx, void* workspace, size_t workspace_bytes,
                                     void* stream) {
-  return tg::launch_select_gather(n, scores, doc_begin, doc_end, k, kept_idx, nullptr, TG_BF16, 0, nullptr, 0,
-                                  nullptr, 0, workspace, workspace_bytes, stream);
+  // the three-digit kernel: measured faster for the selection alone than sel_gather_kernel
+  const tg::SelKeys src{scores, 0ull, 0};
+  return tg::launch_select(n, src, doc_begin, doc_end, &k, 1, kept_idx, workspace, workspace_bytes, stream);
 }
 
 extern "C" tg_status tg_select_gather(int32_t dtype, int64_t n, int32_t d_model, const float* scores,

@@ -139,15 +139,29 @@ def test_given_up_wait_is_reported_and_sticky():
 
 
 def test_workspace_not_zero_filled_is_reported():
-    """A workspace whose histogram is not zero (never zero-filled) is detected: the coarse
-    histogram's total differs from the document length, and the call reports failure
-    instead of selecting from a corrupt histogram."""
+    """A workspace whose histogram is not zero (never zero-filled) is detected: a digit's
+    histogram no longer sums to the keys it must hold, and the call reports failure
+    instead of selecting from a corrupt histogram.  Both selection kernels are covered:
+    the three-digit one (first-digit histogram at byte 64, a later digit's after it) and
+    the one that also gathers (coarse histogram at byte 110848)."""
     binding = require_gpu()
     import torch
     n, b, e, k = 50000, 0, 49000, 3000
     st = torch.from_numpy(np.random.default_rng(12).normal(size=n).astype(np.float32)).cuda()
+    xt = torch.randn(n, 64, dtype=torch.bfloat16, device="cuda")
     ws = torch.zeros(binding.tg_select_workspace_bytes(n), dtype=torch.uint8, device="cuda")
-    ws[110848:110848 + 1024] = 1   # the coarse histogram's bytes
-    binding.tg_select_topk(st, b, e, k, workspace=ws)
-    with pytest.raises(binding.TokenGateError):
-        binding.tg_select_check(ws)
+    for lo, call in ((64, "topk"), (64 + 2048 * 4, "topk"), (64, "multi"), (110848, "gather")):
+        ws.zero_()
+        ws[lo:lo + 1024] = 1
+        kept = torch.full((binding.tg_num_kept(n, b, e, k),), -1, dtype=torch.int32, device="cuda")
+        if call == "topk":
+            binding.tg_select_topk(st, b, e, k, out=kept, workspace=ws)
+        elif call == "multi":
+            binding.tg_select_topk_multi(st, b, e, [k, 7], workspace=ws)
+        else:
+            binding.tg_select_gather(st, xt, b, e, k, kept=kept, workspace=ws)
+        with pytest.raises(binding.TokenGateError) as err:
+            binding.tg_select_check(ws)
+        assert err.value.status == 5, (lo, call)
+        if call != "multi":
+            assert int((kept != -1).sum()) == 0, (lo, call)   # nothing was written
