@@ -23,8 +23,9 @@
 //    rotation is element-wise in registers.  Both operands stream through an NS-stage
 //    LDS ring by DMA (64-wide k-chunks, 128-byte rows XOR-swizzled by (row >> 1) & 7 so
 //    the operand reads are conflict-free); the epilogue adds the bias, rotates q and k
-//    with the table and writes bf16 rows through LDS, so each row leaves as whole lines.  Feature tiles are spread so that each XCD
-//    keeps the same two W tiles in its L2 while the token tiles stream past.
+//    with the table and writes bf16 rows through LDS, so each row leaves as whole lines.  The
+//    tile grid is dealt to the XCDs in blocks that minimise the operand tiles each XCD's L2
+//    must fetch.
 #include <type_traits>
 
 #include "tg_common.h"
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(kQkvWaves * 64, 1) void qkv_rope_kernel(
     int m, int d_model, const uint16_t* __restrict__ x, int64_t ldx, const uint16_t* __restrict__ w,
     const float* __restrict__ bias, int n_feat, int hq, int hkv, const float2* __restrict__ tab,
     uint16_t* __restrict__ q_out, uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, int64_t slot0,
-    int n_ft) {
+    int n_ft, int n_tt, int fb) {
   using T = QkvTile<BTW, NS>;
   constexpr int BT = T::BT, AT = T::AT, WT = T::WT;
   constexpr int HT = D / 64;                 // 32-wide accumulator tiles per half head
@@ -102,11 +103,22 @@ __global__ __launch_bounds__(kQkvWaves * 64, 1) void qkv_rope_kernel(
   // SIMDs, so a ragged last token tile (only its first slices hold tokens) costs less
   const int wh = wave % T::WH, wt = wave / T::WH;
 
-  // workgroup -> (feature tile, token tile): with n_ft a multiple of 8, consecutive
-  // workgroups (which the dispatcher sends to the 8 XCDs in turn) take different
-  // feature tiles and each XCD only ever sees n_ft / 8 of them
+  // workgroup -> (feature tile, token tile).  The dispatcher sends consecutive workgroups to
+  // the 8 XCDs in turn, and an XCD runs about 32 of them at once (one per CU), which share
+  // its L2.  With fb > 0 the tile grid is cut into blocks of fb feature tiles x 32 / fb
+  // token tiles and each block goes whole to one XCD: its 32 workgroups fetch fb + 32 / fb
+  // operand tiles (12 for fb = 4) instead of the 18 of 2 feature tiles x 16 token tiles.
+  // Otherwise (grids too small to give every XCD two blocks), with n_ft a multiple of 8,
+  // each XCD only ever sees n_ft / 8 feature tiles while the token tiles stream past.
   int ft, tt;
-  if (n_ft % 8 == 0) {
+  if (fb > 0) {
+    const int tb = 32 / fb, n_fb = n_ft / fb;
+    const int xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const int blk = (j / 32) * 8 + xcd, loc = j % 32;
+    ft = (blk % n_fb) * fb + loc % fb;
+    tt = (blk / n_fb) * tb + loc / fb;
+    if (blk >= n_fb * ((n_tt + tb - 1) / tb) || tt >= n_tt) return;   // padding of the last blocks
+  } else if (n_ft % 8 == 0) {
     const int per = n_ft / 8, xcd = blockIdx.x % 8, j = blockIdx.x / 8;
     ft = xcd * per + j % per;
     tt = j / per;
@@ -291,10 +303,16 @@ static tg_status launch_qkv(int m, int d_model, const void* x, int64_t ldx, cons
   const int n_feat = (hq + 2 * hkv) * D;
   const int n_ft = (n_feat + kQkvFeat - 1) / kQkvFeat;
   const int n_tt = (m + BT - 1) / BT;
-  hipLaunchKernelGGL((qkv_rope_kernel<D, BTW, NS>), dim3(n_ft * n_tt), dim3(kQkvWaves * 64), 0, st, m, d_model,
+  // XCD blocks (see the kernel) when every XCD gets at least two of them
+  const int fb = n_ft % 4 == 0 ? 4 : (n_ft % 2 == 0 ? 2 : 1);
+  const int64_t n_blocks = (int64_t)(n_ft / fb) * ((n_tt + 32 / fb - 1) / (32 / fb));
+  const bool blocked = n_blocks >= 16;
+  const int64_t grid = blocked ? 8 * 32 * ((n_blocks + 7) / 8) : (int64_t)n_ft * n_tt;
+  if (grid > INT32_MAX) return TG_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((qkv_rope_kernel<D, BTW, NS>), dim3((unsigned)grid), dim3(kQkvWaves * 64), 0, st, m, d_model,
                      static_cast<const uint16_t*>(x), ldx, static_cast<const uint16_t*>(w), bias, n_feat, hq, hkv,
                      tab, static_cast<uint16_t*>(q_out), static_cast<uint16_t*>(k_cache),
-                     static_cast<uint16_t*>(v_cache), slot0, n_ft);
+                     static_cast<uint16_t*>(v_cache), slot0, n_ft, n_tt, blocked ? fb : 0);
   TG_CHECK_LAUNCH();
   return TG_OK;
 }

@@ -37,6 +37,10 @@ CASES = [
     (300, 256, 4, 2, 128, False, 0, 10),
     (333, 192, 6, 1, 64, True, 17, 0),
     (517, 512, 16, 8, 128, True, 100, 83),
+    # grids large enough for the XCD-blocked tile order: 8 feature tiles x 57 token tiles
+    # (ragged last block), and 3 feature tiles (the last half empty) x 162 token tiles
+    (14500, 64, 8, 4, 128, True, 11, 4),
+    (41300, 64, 3, 1, 128, False, 0, 0),
 ]
 
 
