@@ -158,7 +158,7 @@ tg_status tg_select_gather(int32_t dtype, int64_t n, int32_t d_model, const floa
  * tg_select_gather_noalloc -- tg_select_gather without a workspace argument, for callers
  * that cannot allocate device memory: code under HIP graph capture, serving loops that
  * must not call hipMalloc, harnesses that forbid allocation.  The workspace is a static
- * device array of tg_select_workspace_bytes' fixed size (217 KiB, enough for every n: the
+ * device array of tg_select_workspace_bytes' fixed size (218 KiB, enough for every n: the
  * selection's layout does not depend on n), one per device, held by the library until the
  * process ends.  Each call clears it on `stream` with a small fill kernel before selecting,
  * so a call that gave up leaves nothing behind for the next.  Calls that overlap on one

@@ -15,9 +15,11 @@
 // word, its workgroup stops, and every later selection on that workspace exits at
 // once until the caller zero-fills it again (tg_select_check reports the word).
 //
-// sel_gather_kernel -- one budget (tg_select_topk), optionally with the gather of
-// the kept rows fused in (tg_select_gather).  Up to 512 workgroups of 256 threads
-// each own a chunk of positions, their keys held in registers.  Two barriers:
+// sel_gather_kernel -- one budget with the gather of the kept rows fused in
+// (tg_select_gather, tg_select_gather_noalloc).  At most 64 selection workgroups of 256
+// threads each own a chunk of positions, their keys held in registers; the rest of a
+// grid of up to 512 workgroups are helpers that only copy rows.  Two barriers among the
+// selection workgroups:
 //   1. each workgroup histograms its document keys over the top 8 bits (coarse) and
 //      the top 14 bits (fine) in LDS and merges the non-zero bins into global
 //      histograms;  [barrier]
@@ -34,15 +36,16 @@
 //      without another exchange: position i is kept iff it is sure, or a candidate
 //      with key > T, or key == T with fewer than need_eq equal keys before it, and its
 //      slot is (kept-outright positions before i) + min(equal keys before i, need_eq);
-//   4. the gather: workgroup w copies the rows of output slots [w M / G, (w+1) M / G),
-//      balanced however the kept positions cluster, after waiting for the ready flags
-//      of the one or two chunks whose owners wrote those slots' indices.
+//   4. the gather: chunk w's owner publishes its first output slot and slot count on
+//      its flag line, and the owner and its helpers (the team of chunk w) copy those
+//      rows, each a share of them, after waiting for the flag.
 // If the threshold's fine bin holds more candidates than fit in LDS (heavy ties),
 // steps 2-3 fall back to two more radix passes over global histograms and one more
 // exchange of per-chunk counts (three more barriers), with the same result.
 //
-// sel_fused_kernel -- several budgets in one launch (tg_select_topk_multi) and the
-// random selector (tg_select_random).  At most 64 workgroups of 512 threads; radix
+// sel_fused_kernel -- one budget (tg_select_topk; faster than the kernel above when the
+// gather runs as its own launch), several budgets in one launch (tg_select_topk_multi)
+// and the random selector (tg_select_random).  At most 64 workgroups of 512 threads; radix
 // select over three digits (bits 31..21, 20..10, 9..0), each a histogram merged with
 // atomics and a barrier, then the counts of kept-outright and equal-to-T positions
 // are exchanged at one more barrier and every workgroup compacts its chunk.  The

@@ -79,12 +79,12 @@ def assert_workspace_clean(ws):
     (barrier and exit counters, failure word, spin bound, candidate count: bytes 0..19), the
     several-budget kernel's digit histograms (bytes 64 .. 106560: 2048 bins shared, then
     2048 and 1024 bins for each of up to 8 budgets), the one-budget kernel's coarse, fine and
-    two digit histograms (bytes 110848 .. 179456: 256 + 16384 + 512 + 512 bins) and the ready
-    flags of its 64 chunks (the first word of each 128-byte line from byte 179456)."""
+    two digit histograms (bytes 110848 .. 181504: 256 + 16384 + 512 + 512 bins) and the ready
+    flags of its 64 chunks (the first word of each 128-byte line from byte 181504)."""
     assert int(ws[:20].count_nonzero()) == 0
     assert int(ws[64:106560].count_nonzero()) == 0
-    assert int(ws[110848:179456].count_nonzero()) == 0
-    ready = ws[179456:179456 + 64 * 128].view(64, 128)[:, :4]
+    assert int(ws[110848:181504].count_nonzero()) == 0
+    ready = ws[181504:181504 + 64 * 128].view(64, 128)[:, :4]
     assert int(ready.count_nonzero()) == 0
 
 
