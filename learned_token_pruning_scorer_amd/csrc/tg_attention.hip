@@ -304,14 +304,14 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       uint32_t hh = 0, ll = 0;
-      if (BIAS) {
+      if (BIAS) {   // the score as two bf16 parts, each in both halves of a word
         const float sr = *reinterpret_cast<const float*>(lds + 4 * l32 + (C::SB + buf * kBN * 4 + kt * 128));
-        const __bf16 s_hi = static_cast<__bf16>(sr);
-        const __bf16 s_lo = static_cast<__bf16>(sr - static_cast<float>(s_hi));
-        hh = (uint32_t)__builtin_bit_cast(uint16_t, s_hi) * 0x10001u;
-        ll = (uint32_t)__builtin_bit_cast(uint16_t, s_lo) * 0x10001u;
+        hh = pack_bf16x2(sr, sr);
+        ll = pack_bf16x2(sr - __uint_as_float(hh & 0xffff0000u), sr - __uint_as_float(hh & 0xffff0000u));
       }
-      const u32x4 e = {half == 0 ? hh : 0u, half == 0 ? ll : 0u, half == 0 ? 0x3f80u : 0u, 0u};   // 1.0 at k = 4
+      // 1.0 at k = 4.  The upper lane half holds k = 8..15, where the B operand is zero, so its
+      // (finite) values add nothing and need no masking.
+      const u32x4 e = {hh, ll, 0x3f80u, 0u};
       sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, e), qext, sacc[kt], 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(2);   // vector phase (mask, max, exp, pack) goes first
@@ -328,11 +328,14 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
             if (kp[r] > qpos || kb + kk + r >= m) sacc[kt][4 * g + r] = -INFINITY;
         }
     }
-    float mt = fmaxf(sacc[0][0], sacc[0][1]);
+    // a serial chain of three-input maxima (v_max3_f32): 16 instructions for 32 values
+    float mt = fmaxf(fmaxf(sacc[0][0], sacc[0][1]), sacc[0][2]);
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) mt = fmaxf(mt, fmaxf(sacc[0][i], sacc[0][i + 1]));
+    for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sacc[0][i]), sacc[0][i + 1]);
+    mt = fmaxf(fmaxf(mt, sacc[0][15]), sacc[1][0]);
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(sacc[1][i], sacc[1][i + 1]));
+    for (int i = 1; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sacc[1][i]), sacc[1][i + 1]);
+    mt = fmaxf(mt, sacc[1][15]);
     // V^T operands of the first d tile: read now, consumed after the softmax
     u32x2 vpre[4][2];
 #pragma unroll
