@@ -38,6 +38,8 @@
 //  * reduce: sums the partials of ds (over key/value heads), dgain and dtau in a fixed
 //         order, so results are deterministic.
 // Every gradient element is written by exactly one workgroup: no float atomics.
+#include <type_traits>
+
 #include "tg_common.h"
 
 namespace tg {
@@ -236,23 +238,32 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
         sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(k_t, 32 * h2 + l32, s, half), qf[s], sa, 0, 0, 0);
         da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(v_t, 32 * h2 + l32, s, half), df[s], da, 0, 0, 0);
       }
-      // register e holds key kb2 + 8 (e/4) + 4 half + e%4, query = this lane's row
+      // register e holds key kb2 + 8 (e/4) + 4 half + e%4, query = this lane's row.  The mask
+      // is needed only where a key may follow a query (positions rise with the index) or a key
+      // or query lies past the end; elsewhere every key is visible (uniform over the wave).
+      const bool masked = kb2 + 31 > q0 || kb2 + 32 > m || q0 + 32 > m;
+      auto dz = [&](auto maskc) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j0 = 32 * h2 + 8 * g + 4 * half;
-        f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-        if (s_kept) sv = *reinterpret_cast<const f32x4*>(&s_t[j0]);
-        i32x4 kp;
-        if (pos) kp = *reinterpret_cast<const i32x4*>(&p_t[j0]);
-        else kp = i32x4{kb + j0, kb + j0 + 1, kb + j0 + 2, kb + j0 + 3};
+        for (int g = 0; g < 4; ++g) {
+          const int j0 = 32 * h2 + 8 * g + 4 * half;
+          f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+          if (s_kept) sv = *reinterpret_cast<const f32x4*>(&s_t[j0]);
+          i32x4 kp = {};
+          if (decltype(maskc)::value) {
+            if (pos) kp = *reinterpret_cast<const i32x4*>(&p_t[j0]);
+            else kp = i32x4{kb + j0, kb + j0 + 1, kb + j0 + 2, kb + j0 + 3};
+          }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = 4 * g + r;
-          const bool vis = kp[r] <= qpos && kb + j0 + r < m;
-          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sa[e], c2, fmaf(g2, sv[r], nlse2))) : 0.f;
-          da[e] = p * (da[e] - dval);   // da now holds dZ
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * g + r;
+            const bool vis = !decltype(maskc)::value || (kp[r] <= qpos && kb + j0 + r < m);
+            const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sa[e], c2, fmaf(g2, sv[r], nlse2))) : 0.f;
+            da[e] = p * (da[e] - dval);   // da now holds dZ
+          }
         }
-      }
+      };
+      if (masked) dz(std::true_type{});
+      else dz(std::false_type{});
       const bf16x8 z0 = pack_acc(da, 0), z1 = pack_acc(da, 1);
 #pragma unroll
       for (int u = 0; u < D / 32; ++u) {
@@ -426,21 +437,30 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
           da[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwd_row16<D>(o_t, 16 * b + l16, s, grp), vf[s], da[b], 0, 0,
                                                           0);
         }
-      // register i of block b holds query qb + 16 b + 4 G + i, key = this lane's
+      // register i of block b holds query qb + 16 b + 4 G + i, key = this lane's.  The mask is
+      // needed only where a query may precede a key of this wave or a key or query lies past
+      // the end; elsewhere every pair is visible (uniform over the wave).
+      const bool masked = qb < kw0 + 15 || qb + kDkvRows > m || kw0 + 16 > m;
       f32x4_t p[2];
+      auto probs = [&](auto maskc) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int i0 = 16 * b + 4 * grp;
-        const f32x4_t lv = *reinterpret_cast<const f32x4_t*>(&lse_t[i0]);
-        i32x4 qp;
-        if (pos) qp = *reinterpret_cast<const i32x4*>(&p_t[i0]);
-        else qp = i32x4{qb + i0, qb + i0 + 1, qb + i0 + 2, qb + i0 + 3};
+        for (int b = 0; b < 2; ++b) {
+          const int i0 = 16 * b + 4 * grp;
+          const f32x4_t lv = *reinterpret_cast<const f32x4_t*>(&lse_t[i0]);
+          i32x4 qp = {};
+          if (decltype(maskc)::value) {
+            if (pos) qp = *reinterpret_cast<const i32x4*>(&p_t[i0]);
+            else qp = i32x4{qb + i0, qb + i0 + 1, qb + i0 + 2, qb + i0 + 3};
+          }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool vis = kpos <= qp[i] && qb + i0 + i < m;
-          p[b][i] = vis ? __builtin_amdgcn_exp2f(fmaf(sa[b][i], c2, bias2 - lv[i])) : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            const bool vis = !decltype(maskc)::value || (kpos <= qp[i] && qb + i0 + i < m);
+            p[b][i] = vis ? __builtin_amdgcn_exp2f(fmaf(sa[b][i], c2, bias2 - lv[i])) : 0.f;
+          }
         }
-      }
+      };
+      if (masked) probs(std::true_type{});
+      else probs(std::false_type{});
       const bf16x8 pb = pack8(p[0], p[1]);
 #pragma unroll
       for (int t2 = 0; t2 < DT; ++t2)
