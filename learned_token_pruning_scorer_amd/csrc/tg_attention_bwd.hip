@@ -104,6 +104,17 @@ __device__ __forceinline__ bf16x8 bwd_tr(const uint16_t* tile, int r0, int s2, i
   return __builtin_bit_cast(bf16x8, a4);
 }
 
+// Operand reads at a precomputed per-lane byte offset from a tile's LDS base: the offsets of
+// the swizzled layouts depend only on the lane and the k-step or d tile, so they are formed
+// once per kernel and every read is one base + offset address (plus an immediate).
+__device__ __forceinline__ bf16x8 lds_row(const char* base, uint32_t off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+__device__ __forceinline__ u32x2 lds_tr(const char* base, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) bs16x4*)(base + off)));
+}
+
 // bf16 B operand of the 16-row k-step s2 from a 32x32 accumulator
 __device__ __forceinline__ bf16x8 pack_acc(const f32x16& a, int s2) {
   u32x4 w;
@@ -198,6 +209,24 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqa[u][i] = 0.f;
 
+  // byte offsets within a 32-key half tile: K / V rows (A operand of S^T and dP^T, k-step s)
+  // and K^T (A operand of dQ^T, d tile u, the lane's first or second 8-key group g8)
+  uint32_t rowo[D / 16], tro[D / 32][2];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) rowo[s] = (uint32_t)(2 * (l32 * D + 8 * ((2 * s + half) ^ bwd_swz<D>(l32))));
+  {
+    const int gi = lane & 15, gg = lane >> 4;
+    const int row_lane = 4 * half + (gi >> 2);
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+      for (int g8 = 0; g8 < 2; ++g8) {
+        const int row = 8 * g8 + row_lane;
+        const int dcol = 32 * u + 16 * (gg & 1) + 4 * (gi & 3);
+        tro[u][g8] = (uint32_t)(2 * (row * D + 8 * ((dcol >> 3) ^ bwd_swz<D>(row)) + (dcol & 7)));
+      }
+  }
+
   const int rows_end = min(m, (qt + 1) * ROWS);
   const int n_tiles = (rows_end + kDqKeys - 1) / kDqKeys;
   const uint16_t* kh = k + (int64_t)kvh * D;
@@ -230,13 +259,15 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
     for (int h2 = 0; h2 < kDqKeys / 32; ++h2) {
       const int kb2 = kb + 32 * h2;
       if (kb2 > wave_last) break;
+      const char* kh2 = reinterpret_cast<const char*>(k_t) + h2 * 32 * D * 2;   // this half's 32 keys
+      const char* vh2 = reinterpret_cast<const char*>(v_t) + h2 * 32 * D * 2;
       f32x16 sa, da;
 #pragma unroll
       for (int i = 0; i < 16; ++i) { sa[i] = 0.f; da[i] = 0.f; }
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(k_t, 32 * h2 + l32, s, half), qf[s], sa, 0, 0, 0);
-        da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row<D>(v_t, 32 * h2 + l32, s, half), df[s], da, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(kh2, rowo[s]), qf[s], sa, 0, 0, 0);
+        da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(vh2, rowo[s]), df[s], da, 0, 0, 0);
       }
       // register e holds key kb2 + 8 (e/4) + 4 half + e%4, query = this lane's row.  The mask
       // is needed only where a key may follow a query (positions rise with the index) or a key
@@ -266,10 +297,15 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
       else dz(std::false_type{});
       const bf16x8 z0 = pack_acc(da, 0), z1 = pack_acc(da, 1);
 #pragma unroll
-      for (int u = 0; u < D / 32; ++u) {
-        dqa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(k_t, 32 * h2, 0, u, lane), z0, dqa[u], 0, 0, 0);
-        dqa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr<D>(k_t, 32 * h2, 1, u, lane), z1, dqa[u], 0, 0, 0);
-      }
+      for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {   // keys 16 s2 .. 16 s2 + 15 of the half
+          const u32x2 p0 = lds_tr(kh2 + s2 * 16 * D * 2, tro[u][0]);
+          const u32x2 p1 = lds_tr(kh2 + s2 * 16 * D * 2, tro[u][1]);
+          const u32x4 a4 = {p0[0], p0[1], p1[0], p1[1]};
+          dqa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), s2 == 0 ? z0 : z1, dqa[u],
+                                                           0, 0, 0);
+        }
     }
   }
   if (live_row) {
@@ -373,6 +409,19 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
     for (int i = 0; i < 4; ++i) { dka[t][i] = 0.f; dva[t][i] = 0.f; }
   float ds_acc = 0.f, dtau_acc = 0.f;
 
+  // byte offsets within a Q or dO tile: rows (A operand of S and dP, k-step s) and transposed
+  // rows (A operand of dK^T and dV^T, d tile t2); the second 16-row block is 16 rows further
+  uint32_t rowo[KS], tro[DT];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) rowo[s] = (uint32_t)(2 * (l16 * D + 8 * ((4 * s + grp) ^ bwd_swz<D>(l16))));
+#pragma unroll
+  for (int t2 = 0; t2 < DT; ++t2) {
+    const int row = 4 * grp + (l16 >> 2);
+    const int dcol = 16 * t2 + 4 * (l16 & 3);
+    tro[t2] = (uint32_t)(2 * (row * D + 8 * ((dcol >> 3) ^ bwd_swz<D>(row)) + (dcol & 7)));
+  }
+  constexpr uint32_t kBlk16 = 16 * D * 2;         // bytes of 16 rows
+
   const int first_tile = kb0 / kDkvRows;          // queries before the first key see none of them
   const int n_qt = (m + kDkvRows - 1) / kDkvRows;
   const int per_head = n_qt - first_tile;
@@ -401,7 +450,10 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
   for (int i = 0; i < kDkvStages - 1; ++i)
     if (i < n_it) issue(i);
   float col = 0.f;   // this lane's part of the sum over queries of dZ, current head
-  for (int it = 0; it < n_it; ++it) {
+  // one query tile; ST = it mod kDkvStages is a compile-time constant, so the tile's LDS base
+  // and every operand address within it are a per-lane offset plus an immediate
+  auto step = [&](int it, auto stc) {
+    constexpr int ST = decltype(stc)::value;
     const int hh = it / per_head, t = first_tile + it % per_head;
     const int head = kvh * group + hh, qb = t * kDkvRows;
     // tile it has landed once the DMAs of the later tiles already issued are all that remain
@@ -415,7 +467,7 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
     __syncthreads();   // tile it visible to every wave; the buffer of tile it - 1 is free
     if (it + kDkvStages - 1 < n_it) issue(it + kDkvStages - 1);
     if (qb + kDkvRows - 1 >= kw0 && kw0 < m) {   // some query of the tile sees these keys
-      const char* buf = lds + (it % kDkvStages) * L::BUF;
+      const char* buf = lds + ST * L::BUF;   // ST = it mod kDkvStages, a constant here
       const uint16_t* q_t = reinterpret_cast<const uint16_t*>(buf + L::Q0);
       const uint16_t* o_t = reinterpret_cast<const uint16_t*>(buf + L::O0);
       const float* lse_t = reinterpret_cast<const float*>(buf + L::ST0);
@@ -428,14 +480,20 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) { sa[b][i] = 0.f; da[b][i] = 0.f; }
+      const char* qc = reinterpret_cast<const char*>(q_t);
+      const char* oc = reinterpret_cast<const char*>(o_t);
+      // transposed A operand over the tile's 32 rows: rows 4G.. of each 16-row block, d tile t2
+      auto tr_a = [&](const char* tile, int t2) {
+        const u32x2 p0 = lds_tr(tile, tro[t2]), p1 = lds_tr(tile + kBlk16, tro[t2]);
+        const u32x4 a4 = {p0[0], p0[1], p1[0], p1[1]};
+        return __builtin_bit_cast(bf16x8, a4);
+      };
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          sa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwd_row16<D>(q_t, 16 * b + l16, s, grp), kf[s], sa[b], 0, 0,
-                                                          0);
-          da[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwd_row16<D>(o_t, 16 * b + l16, s, grp), vf[s], da[b], 0, 0,
-                                                          0);
+          sa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row(qc + b * kBlk16, rowo[s]), kf[s], sa[b], 0, 0, 0);
+          da[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row(oc + b * kBlk16, rowo[s]), vf[s], da[b], 0, 0, 0);
         }
       // register i of block b holds query qb + 16 b + 4 G + i, key = this lane's.  The mask is
       // needed only where a query may precede a key of this wave or a key or query lies past
@@ -464,7 +522,7 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       const bf16x8 pb = pack8(p[0], p[1]);
 #pragma unroll
       for (int t2 = 0; t2 < DT; ++t2)
-        dva[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwd_tr16<D>(o_t, t2, lane), pb, dva[t2], 0, 0, 0);
+        dva[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_a(oc, t2), pb, dva[t2], 0, 0, 0);
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(&d_t[16 * b + 4 * grp]);
@@ -479,7 +537,7 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       const bf16x8 zb = pack8(da[0], da[1]);
 #pragma unroll
       for (int t2 = 0; t2 < DT; ++t2)
-        dka[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bwd_tr16<D>(q_t, t2, lane), zb, dka[t2], 0, 0, 0);
+        dka[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_a(qc, t2), zb, dka[t2], 0, 0, 0);
     }
     if (t == n_qt - 1) {
       // this head's key-side sums: the four lane groups hold parts of the same key's column
@@ -492,6 +550,12 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       if (lane == 0) dgain_part[((int64_t)head * n_kblocks + kblk) * kDkvWaves + wave] = gsum;
       col = 0.f;
     }
+    };
+  static_assert(kDkvStages == 3, "the tile loop is unrolled over the three stages");
+  for (int it0 = 0; it0 < n_it; it0 += kDkvStages) {
+    step(it0, std::integral_constant<int, 0>{});
+    if (it0 + 1 < n_it) step(it0 + 1, std::integral_constant<int, 1>{});
+    if (it0 + 2 < n_it) step(it0 + 2, std::integral_constant<int, 2>{});
   }
   if (live_key) {
     if (grp == 0) ds_part[(int64_t)kvh * m + key] = ds_acc;
