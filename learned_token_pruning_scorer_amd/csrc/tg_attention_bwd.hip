@@ -244,69 +244,75 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
   };
 
   if (n_tiles > 0) issue(0);
-  for (int t = 0; t < n_tiles; ++t) {
+  // 32 keys of tile t (half h2 of its 64) from LDS buffer BUF = t mod 2; BUF and h2 are
+  // compile-time constants, so every operand address is a per-lane offset plus an immediate
+  auto half_tile = [&](int kb, auto bufc, auto h2c) {
+    constexpr int BUF = decltype(bufc)::value, h2 = decltype(h2c)::value;
+    const int kb2 = kb + 32 * h2;
+    const char* buf = lds + BUF * L::BUF;
+    const float* s_t = reinterpret_cast<const float*>(buf + L::S0);
+    const int32_t* p_t = reinterpret_cast<const int32_t*>(buf + L::P0);
+    const char* kh2 = buf + L::K0 + h2 * 32 * D * 2;   // this half's 32 keys
+    const char* vh2 = buf + L::V0 + h2 * 32 * D * 2;
+    f32x16 sa, da;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { sa[i] = 0.f; da[i] = 0.f; }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(kh2, rowo[s]), qf[s], sa, 0, 0, 0);
+      da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(vh2, rowo[s]), df[s], da, 0, 0, 0);
+    }
+    // register e holds key kb2 + 8 (e/4) + 4 half + e%4, query = this lane's row.  The mask
+    // is needed only where a key may follow a query (positions rise with the index) or a key
+    // or query lies past the end; elsewhere every key is visible (uniform over the wave).
+    const bool masked = kb2 + 31 > q0 || kb2 + 32 > m || q0 + 32 > m;
+    auto dz = [&](auto maskc) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int j0 = 32 * h2 + 8 * g + 4 * half;
+        f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+        if (s_kept) sv = *reinterpret_cast<const f32x4*>(&s_t[j0]);
+        i32x4 kp = {};
+        if (decltype(maskc)::value) {
+          if (pos) kp = *reinterpret_cast<const i32x4*>(&p_t[j0]);
+          else kp = i32x4{kb + j0, kb + j0 + 1, kb + j0 + 2, kb + j0 + 3};
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = 4 * g + r;
+          const bool vis = !decltype(maskc)::value || (kp[r] <= qpos && kb + j0 + r < m);
+          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sa[e], c2, fmaf(g2, sv[r], nlse2))) : 0.f;
+          da[e] = p * (da[e] - dval);   // da now holds dZ
+        }
+      }
+    };
+    if (masked) dz(std::true_type{});
+    else dz(std::false_type{});
+    const bf16x8 z0 = pack_acc(da, 0), z1 = pack_acc(da, 1);
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {   // keys 16 s2 .. 16 s2 + 15 of the half
+        const u32x2 p0 = lds_tr(kh2 + s2 * 16 * D * 2, tro[u][0]);
+        const u32x2 p1 = lds_tr(kh2 + s2 * 16 * D * 2, tro[u][1]);
+        const u32x4 a4 = {p0[0], p0[1], p1[0], p1[1]};
+        dqa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), s2 == 0 ? z0 : z1, dqa[u],
+                                                         0, 0, 0);
+      }
+  };
+  auto step = [&](int t, auto bufc) {
     const int kb = t * kDqKeys;
     dma_wait_all();
     __syncthreads();   // tile t visible to every wave; tile t - 1's buffer free
     if (t + 1 < n_tiles) issue(t + 1);
-    if (!wave_live || kb > wave_last) continue;
-    const char* buf = lds + (t & 1) * L::BUF;
-    const uint16_t* k_t = reinterpret_cast<const uint16_t*>(buf + L::K0);
-    const uint16_t* v_t = reinterpret_cast<const uint16_t*>(buf + L::V0);
-    const float* s_t = reinterpret_cast<const float*>(buf + L::S0);
-    const int32_t* p_t = reinterpret_cast<const int32_t*>(buf + L::P0);
-#pragma unroll 1
-    for (int h2 = 0; h2 < kDqKeys / 32; ++h2) {
-      const int kb2 = kb + 32 * h2;
-      if (kb2 > wave_last) break;
-      const char* kh2 = reinterpret_cast<const char*>(k_t) + h2 * 32 * D * 2;   // this half's 32 keys
-      const char* vh2 = reinterpret_cast<const char*>(v_t) + h2 * 32 * D * 2;
-      f32x16 sa, da;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) { sa[i] = 0.f; da[i] = 0.f; }
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(kh2, rowo[s]), qf[s], sa, 0, 0, 0);
-        da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(vh2, rowo[s]), df[s], da, 0, 0, 0);
-      }
-      // register e holds key kb2 + 8 (e/4) + 4 half + e%4, query = this lane's row.  The mask
-      // is needed only where a key may follow a query (positions rise with the index) or a key
-      // or query lies past the end; elsewhere every key is visible (uniform over the wave).
-      const bool masked = kb2 + 31 > q0 || kb2 + 32 > m || q0 + 32 > m;
-      auto dz = [&](auto maskc) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int j0 = 32 * h2 + 8 * g + 4 * half;
-          f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-          if (s_kept) sv = *reinterpret_cast<const f32x4*>(&s_t[j0]);
-          i32x4 kp = {};
-          if (decltype(maskc)::value) {
-            if (pos) kp = *reinterpret_cast<const i32x4*>(&p_t[j0]);
-            else kp = i32x4{kb + j0, kb + j0 + 1, kb + j0 + 2, kb + j0 + 3};
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 4 * g + r;
-            const bool vis = !decltype(maskc)::value || (kp[r] <= qpos && kb + j0 + r < m);
-            const float p = vis ? __builtin_amdgcn_exp2f(fmaf(sa[e], c2, fmaf(g2, sv[r], nlse2))) : 0.f;
-            da[e] = p * (da[e] - dval);   // da now holds dZ
-          }
-        }
-      };
-      if (masked) dz(std::true_type{});
-      else dz(std::false_type{});
-      const bf16x8 z0 = pack_acc(da, 0), z1 = pack_acc(da, 1);
-#pragma unroll
-      for (int u = 0; u < D / 32; ++u)
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {   // keys 16 s2 .. 16 s2 + 15 of the half
-          const u32x2 p0 = lds_tr(kh2 + s2 * 16 * D * 2, tro[u][0]);
-          const u32x2 p1 = lds_tr(kh2 + s2 * 16 * D * 2, tro[u][1]);
-          const u32x4 a4 = {p0[0], p0[1], p1[0], p1[1]};
-          dqa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), s2 == 0 ? z0 : z1, dqa[u],
-                                                           0, 0, 0);
-        }
-    }
+    if (!wave_live || kb > wave_last) return;
+    half_tile(kb, bufc, std::integral_constant<int, 0>{});
+    if (kb + 32 <= wave_last) half_tile(kb, bufc, std::integral_constant<int, 1>{});
+  };
+  static_assert(kDqKeys == 64, "two 32-key halves per tile");
+  for (int t0 = 0; t0 < n_tiles; t0 += 2) {
+    step(t0, std::integral_constant<int, 0>{});
+    if (t0 + 1 < n_tiles) step(t0 + 1, std::integral_constant<int, 1>{});
   }
   if (live_row) {
     uint16_t* orow = dq + ((int64_t)row * hq + head) * D;
