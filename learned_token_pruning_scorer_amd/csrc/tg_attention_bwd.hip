@@ -27,7 +27,7 @@
 //         query), and dQ^T += K^T dZ^T reads K^T from the tile with ds_read_b64_tr_b16;
 //  * dkv: the transpose, on 16x16x32 MFMA -- a workgroup (8 waves, two per SIMD) owns
 //         128 keys of one key/value head and a wave 16 of them, with K and V as fixed B
-//         operands in registers and the dK / dV accumulators beside them (about 220
+//         operands in registers and the dK / dV accumulators beside them (about 210
 //         registers with the compiler's prefetching, which still lets two waves share
 //         a SIMD and hide each other's latencies);
 //         32-query Q / dO tiles of every head of the group stream through a 3-stage LDS
@@ -37,7 +37,11 @@
 //         per-wave partials;
 //  * reduce: sums the partials of ds (over key/value heads), dgain and dtau in a fixed
 //         order, so results are deterministic.
-// Every gradient element is written by exactly one workgroup: no float atomics.
+// Every gradient element is written by exactly one workgroup: no float atomics.  Both
+// gradient kernels apply the visibility mask only on tiles where a key can follow a query
+// or a row lies past the end, and address every LDS operand by a per-lane offset formed
+// once plus an immediate (their tile loops are unrolled over the LDS buffers): the vector
+// work per tile is otherwise comparable to the MFMA work.
 #include <type_traits>
 
 #include "tg_common.h"
@@ -76,32 +80,6 @@ __device__ __forceinline__ void bwd_dma_tile(uint32_t dst, const uint16_t* __res
     const uint32_t off = (uint32_t)(((int64_t)rr * ld + 8 * (p ^ bwd_swz<D>(r))) * 2);
     dma_lds16(off, base, dst + I * 1024);
   }
-}
-
-// A-operand (row) read: row r of a swizzled tile, 16-wide k-step s, lane half h
-template <int D>
-__device__ __forceinline__ bf16x8 bwd_row(const uint16_t* tile, int r, int s, int half) {
-  return *reinterpret_cast<const bf16x8*>(&tile[r * D + 8 * ((2 * s + half) ^ bwd_swz<D>(r))]);
-}
-
-// Transposed A operand over the tile's rows r0 + 16 s2 .. + 15 and d tile u: lane half
-// h receives rows {4h..4h+3, 8+4h..8+4h+3} (+ r0 + 16 s2), the order in which a 32x32
-// accumulator's registers leave them, at d = 32u + (lane & 31)
-template <int D>
-__device__ __forceinline__ bf16x8 bwd_tr(const uint16_t* tile, int r0, int s2, int u, int lane) {
-  const int half = lane >> 5, gi = lane & 15, gg = lane >> 4;
-  const int row_lane = 4 * half + (gi >> 2);
-  const int dcol = 32 * u + 16 * (gg & 1) + 4 * (gi & 3);
-  u32x2 part[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int row = r0 + 16 * s2 + 8 * r + row_lane;
-    const int off = row * D + 8 * ((dcol >> 3) ^ bwd_swz<D>(row)) + (dcol & 7);
-    part[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                            (__attribute__((address_space(3))) bs16x4*)(&tile[off])));
-  }
-  const u32x4 a4 = {part[0][0], part[0][1], part[1][0], part[1][1]};
-  return __builtin_bit_cast(bf16x8, a4);
 }
 
 // Operand reads at a precomputed per-lane byte offset from a tile's LDS base: the offsets of
@@ -209,8 +187,10 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqa[u][i] = 0.f;
 
-  // byte offsets within a 32-key half tile: K / V rows (A operand of S^T and dP^T, k-step s)
-  // and K^T (A operand of dQ^T, d tile u, the lane's first or second 8-key group g8)
+  // byte offsets within a 32-key half tile: K / V row l32, 16-wide k-step s, lane half h
+  // (A operand of S^T and dP^T), and K^T for d tile u (A operand of dQ^T): lane half h
+  // receives keys {4h..4h+3} (g8 = 0) and {8+4h..8+4h+3} (g8 = 1) of each 16-key step, the
+  // order in which the 32x32 accumulator's registers leave them, at d = 32u + (lane & 31)
   uint32_t rowo[D / 16], tro[D / 32][2];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) rowo[s] = (uint32_t)(2 * (l32 * D + 8 * ((2 * s + half) ^ bwd_swz<D>(l32))));
@@ -335,31 +315,6 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
 // ---------------------------------------------------------------------------------
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// A-operand row read for the 16x16x32 shape: row r, k-step s (32 wide), lane group G
-template <int D>
-__device__ __forceinline__ bf16x8 bwd_row16(const uint16_t* tile, int r, int s, int grp) {
-  return *reinterpret_cast<const bf16x8*>(&tile[r * D + 8 * ((4 * s + grp) ^ bwd_swz<D>(r))]);
-}
-
-// Transposed A operand for the 16x16x32 shape over a 32-row tile: lane group G receives
-// rows {4G..4G+3, 16+4G..16+4G+3}, the rows a 16x16 result leaves in its two row blocks,
-// at d = 16 t + (lane & 15)
-template <int D>
-__device__ __forceinline__ bf16x8 bwd_tr16(const uint16_t* tile, int t, int lane) {
-  const int grp = lane >> 4, gi = lane & 15;
-  const int dcol = 16 * t + 4 * (gi & 3);
-  u32x2 part[2];
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int row = 16 * r + 4 * grp + (gi >> 2);
-    const int off = row * D + 8 * ((dcol >> 3) ^ bwd_swz<D>(row)) + (dcol & 7);
-    part[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                            (__attribute__((address_space(3))) bs16x4*)(&tile[off])));
-  }
-  const u32x4 a4 = {part[0][0], part[0][1], part[1][0], part[1][1]};
-  return __builtin_bit_cast(bf16x8, a4);
-}
-
 __device__ __forceinline__ bf16x8 pack8(const f32x4_t& a, const f32x4_t& b) {
   const u32x4 w = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
   return __builtin_bit_cast(bf16x8, w);
@@ -415,8 +370,10 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
     for (int i = 0; i < 4; ++i) { dka[t][i] = 0.f; dva[t][i] = 0.f; }
   float ds_acc = 0.f, dtau_acc = 0.f;
 
-  // byte offsets within a Q or dO tile: rows (A operand of S and dP, k-step s) and transposed
-  // rows (A operand of dK^T and dV^T, d tile t2); the second 16-row block is 16 rows further
+  // byte offsets within a Q or dO tile: row l16, 32-wide k-step s, lane group G (A operand
+  // of S and dP), and the transposed read for d tile t2 (A operand of dK^T and dV^T): lane
+  // group G receives rows {4G..4G+3} and, 16 rows further, {16+4G..16+4G+3}, the rows a
+  // 16x16 result leaves in its two row blocks, at d = 16 t2 + (lane & 15)
   uint32_t rowo[KS], tro[DT];
 #pragma unroll
   for (int s = 0; s < KS; ++s) rowo[s] = (uint32_t)(2 * (l16 * D + 8 * ((4 * s + grp) ^ bwd_swz<D>(l16))));
