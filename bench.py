@@ -61,6 +61,8 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true", help="skip the 64k budget sweep against unpruned attention")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the timings of the attention backward and the multi-budget / random selectors")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip timing the library GEMM and torch's causal attention at the step's shapes")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="if > 0: run only this many steps of the main workload (and as many calls of "
                          "each row timed by --no-next's rows), then one streaming copy of CALIB_BYTES "
@@ -321,6 +323,42 @@ def next_rows(path, reps):
     return res
 
 
+def calibration(path, reps):
+    """Library kernels at the step's own shapes, timed beside ours in the same process, as
+    context for the roofline fractions: the scorer's product X . W1^T as a plain library GEMM
+    (torch.nn.functional.linear, bf16 out, no activation, no 1-wide output), and torch's own
+    causal attention (scaled_dot_product_attention, flash backend, no key bias, K/V heads
+    expanded to the query heads) on the step's Q/K/V."""
+    torch, b, w = path.torch, path.b, path.w
+    res = {}
+    try:
+        ours = _event_time_us(torch, lambda: b.tg_gate_score(path.x, path.w1, path.w2, path.b1, path.gi.b2,
+                                                            out=path.scores), reps)
+        lib = _event_time_us(torch, lambda: torch.nn.functional.linear(path.x, path.w1), reps)
+        res["scorer_vs_library_gemm"] = {"us_scorer": ours, "us_library_gemm": lib, "ratio": ours / lib,
+                                         "note": "library GEMM = torch.nn.functional.linear(X, W1) alone"}
+    except Exception as e:   # context only: a library that is missing or fails is reported, not fatal
+        res["scorer_vs_library_gemm"] = {"error": str(e)[:200]}
+    try:
+        import torch.nn.functional as F
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        group = w.n_q_heads // w.n_kv_heads
+        qt = path.q.transpose(0, 1).unsqueeze(0).contiguous()
+        kt = path.kk.transpose(0, 1).repeat_interleave(group, dim=0).unsqueeze(0).contiguous()
+        vt = path.v.transpose(0, 1).repeat_interleave(group, dim=0).unsqueeze(0).contiguous()
+        ours = _event_time_us(torch, lambda: path.attention(), reps)
+        with sdpa_kernel(SDPBackend.FLASH_ATTENTION):
+            lib = _event_time_us(torch, lambda: F.scaled_dot_product_attention(qt, kt, vt, is_causal=True), reps)
+        res["attention_vs_torch_sdpa"] = {"us_gated_attention": ours, "us_torch_sdpa_flash_causal": lib,
+                                          "ratio": ours / lib, "m": path.m,
+                                          "note": "torch SDPA without the key bias or temperature"}
+        del qt, kt, vt
+    except Exception as e:
+        res["attention_vs_torch_sdpa"] = {"error": str(e)[:200]}
+    torch.cuda.empty_cache()
+    return res
+
+
 def sweep64k(binding, torch, steps, warmup):
     """Budget reuse at 64k: the whole path at each budget against unpruned causal attention
     over all N rows (bias off, tau = 1), the comparison the pruning is for."""
@@ -524,6 +562,11 @@ def main():
         print("[bench] timing the backward and the selector variants", file=sys.stderr, flush=True)
         nxt = next_rows(path, max(5, args.steps // 2))
 
+    cal = None
+    if not args.no_calibration:
+        print("[bench] library GEMM and torch attention at the step's shapes", file=sys.stderr, flush=True)
+        cal = calibration(path, max(5, args.steps // 2))
+
     sweep = None
     if not args.no_sweep:
         print("[bench] 64k budget sweep against unpruned attention", file=sys.stderr, flush=True)
@@ -571,6 +614,7 @@ def main():
         },
         "also": also,
         "next_rows": nxt,
+        "calibration": cal,
         "sweep64k": sweep,
     }
     print(json.dumps(out), flush=True)
