@@ -37,12 +37,16 @@
 //    exceeds it by more than 8 in the base-2 exponent, so P stays below 2^8 and most
 //    tiles skip the O rescale;
 //  * operand reads are issued ahead of the work that waits on them: the first two
-//    k-steps' K operands before the next tile's DMA, the first d tile's V^T
-//    operands before the softmax;
+//    k-steps' K operands before the next tile's DMA, the V^T operands of the first
+//    16 keys (every d tile) before the softmax, each next 16 keys' while the
+//    current ones' products run;
+//  * the softmax and the P . V products alternate per 16 keys: the exponentials of
+//    keys 16 (s + 1) .. 16 s + 31 are issued while the four O tiles' products of the
+//    previous 16 keys run (each O tile still accumulates the keys in order);
 //  * a wave raises its issue priority (s_setprio) for the vector phase of a tile (mask,
-//    max, exponentials, packing) and drops it for the MFMA phases, so that of the two
-//    waves sharing a SIMD the one in its softmax goes first while the other's MFMAs run
-//    (about 5% on the 128k workload);
+//    max, exponentials and packing, with the P . V products interleaved) and drops it
+//    for the S products, so that of the two waves sharing a SIMD the one in its softmax
+//    goes first while the other's MFMAs run (about 5% on the 128k workload);
 //  * P^T stays in registers as the B operand of O^T = V^T . P^T; its row sums come
 //    from v_dot2_f32_bf16 on the packed bf16 P that the MFMA consumes.  The V^T
 //    operand is read from the [key][d] tile with ds_read_b64_tr_b16: each 16-lane
@@ -336,14 +340,18 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
 #pragma unroll
     for (int i = 1; i < 15; i += 2) mt = fmaxf(fmaxf(mt, sacc[1][i]), sacc[1][i + 1]);
     mt = fmaxf(mt, sacc[1][15]);
-    // V^T operands of the first d tile: read now, consumed after the softmax
-    u32x2 vpre[4][2];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
+    // V^T operands (ds_read_b64_tr_b16) of d tile u and keys 16 s2 .. 16 s2 + 15
+    auto read_vt = [&](int u, int s2) {
+      u32x2 part[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r)
-        vpre[s2][r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) s16x4*)(lds + va[0] + (C::V0 + buf * C::TILE + (16 * s2 + 8 * r) * D * 2))));
+        part[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(lds + va[u] + (C::V0 + buf * C::TILE + (16 * s2 + 8 * r) * D * 2))));
+      return u32x4{part[0][0], part[0][1], part[1][0], part[1][1]};
+    };
+    u32x4 vcur[D / 32];   // the first 16 keys' operands: read now, consumed after the softmax
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) vcur[u] = read_vt(u, 0);
     mt = pair_max(mt);   // tile max of S - m (base-2 units)
     // first tile: adopt its max; later: move the max only when exceeded by > 2^8
     if (t == tg0 || __ballot(mt > rescale_thr)) {
@@ -363,7 +371,6 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[kt][i] -= delta;
     }
-    bf16x8 pf[4];
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
       u32x4 w;
@@ -376,27 +383,21 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
         if (e2 & 1) l_run2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, l_run2, false);
         else l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), ones, l_run, false);
       }
-      pf[s2] = __builtin_bit_cast(bf16x8, w);
-    }
-    __builtin_amdgcn_s_setprio(0);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
+      u32x4 vnext[D / 32];
+      if (s2 < 3) {
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const u32x4 a4 = {vpre[s2][0][0], vpre[s2][0][1], vpre[s2][1][0], vpre[s2][1][1]};
-      oacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pf[s2], oacc[0], 0, 0, 0);
-    }
+        for (int u = 0; u < D / 32; ++u) vnext[u] = read_vt(u, s2 + 1);
+      }
 #pragma unroll
-    for (int u = 1; u < D / 32; ++u) {
+      for (int u = 0; u < D / 32; ++u)
+        oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vcur[u]), pf, oacc[u], 0, 0, 0);
+      if (s2 < 3) {
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        u32x2 part[2];
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-          part[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) s16x4*)(lds + va[u] + (C::V0 + buf * C::TILE + (16 * s2 + 8 * r) * D * 2))));
-        const u32x4 a4 = {part[0][0], part[0][1], part[1][0], part[1][1]};
-        oacc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), pf[s2], oacc[u], 0, 0, 0);
+        for (int u = 0; u < D / 32; ++u) vcur[u] = vnext[u];
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   wait_dma();
