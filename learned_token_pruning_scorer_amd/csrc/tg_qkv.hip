@@ -26,6 +26,7 @@
 //    with the table and writes bf16 rows through LDS, so each row leaves as whole lines.  The
 //    tile grid is dealt to the XCDs in blocks that minimise the operand tiles each XCD's L2
 //    must fetch.
+#include <atomic>
 #include <type_traits>
 
 #include "tg_common.h"
@@ -317,6 +318,25 @@ static tg_status launch_qkv(int m, int d_model, const void* x, int64_t ldx, cons
   return TG_OK;
 }
 
+// Workgroups of the 256-token projection kernel that the current device runs at once
+// (cached per device; 0 if unknown).
+template <int D>
+static int qkv_slots() {
+  static std::atomic<int> cache[64];
+  int device = 0;
+  if (hipGetDevice(&device) != hipSuccess || device < 0 || device >= 64) return 0;
+  int v = cache[device].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(qkv_rope_kernel<D, 2, 2>),
+                                                   kQkvWaves * 64, 0) != hipSuccess)
+    return 0;
+  v = cus * per_cu;
+  cache[device].store(v, std::memory_order_relaxed);
+  return v;
+}
+
 template <int D>
 static tg_status qkv_rope(int m, int d_model, const void* x, int64_t ldx, const void* w, const float* bias, int hq,
                           int hkv, const int32_t* pos, float theta, void* q_out, void* k_cache, void* v_cache,
@@ -325,7 +345,27 @@ static tg_status qkv_rope(int m, int d_model, const void* x, int64_t ldx, const 
   hipLaunchKernelGGL((rope_table_kernel<D>), dim3((unsigned)((n_tab + 255) / 256)), dim3(256), 0, st, m, pos,
                      std::log2((double)theta), tab, pos_cache, slot0);
   TG_CHECK_LAUNCH();
-  return launch_qkv<D, 2, 2>(m, d_model, x, ldx, w, bias, hq, hkv, tab, q_out, k_cache, v_cache, slot0, st);
+  // A ragged last token tile of r rows keeps only ceil(r / 64) of its four token slices busy
+  // and costs about half a full tile.  When it would run in a round of its own (the full
+  // tiles fill whole rounds of the chip, or leave too little room beside them), its rows go
+  // to a second launch of 128-token tiles, whose waves hold 32 tokens each: twice the busy
+  // waves at half the work each.
+  constexpr int BT = QkvTile<2, 2>::BT;
+  const int r = m % BT, full = m / BT;
+  bool split = false;
+  if (full > 0 && r > 0 && r <= BT / 2) {
+    const int64_t n_ft = ((int64_t)(hq + 2 * hkv) * D + kQkvFeat - 1) / kQkvFeat;
+    const int64_t f = n_ft * full, slots = qkv_slots<D>();
+    if (slots > 0 && f >= slots) split = f % slots == 0 || f % slots + n_ft > slots;
+  }
+  if (!split) return launch_qkv<D, 2, 2>(m, d_model, x, ldx, w, bias, hq, hkv, tab, q_out, k_cache, v_cache, slot0, st);
+  const int m0 = m - r;
+  const tg_status s0 =
+      launch_qkv<D, 2, 2>(m0, d_model, x, ldx, w, bias, hq, hkv, tab, q_out, k_cache, v_cache, slot0, st);
+  if (s0 != TG_OK) return s0;
+  return launch_qkv<D, 1, 3>(r, d_model, static_cast<const uint16_t*>(x) + (int64_t)m0 * ldx, ldx, w, bias, hq, hkv,
+                             tab + (int64_t)m0 * (D / 2), static_cast<uint16_t*>(q_out) + (int64_t)m0 * hq * D,
+                             k_cache, v_cache, slot0 + m0, st);
 }
 
 static size_t rope_table_bytes(int64_t m, int64_t head_dim) {

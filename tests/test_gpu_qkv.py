@@ -41,6 +41,10 @@ CASES = [
     # (ragged last block), and 3 feature tiles (the last half empty) x 162 token tiles
     (14500, 64, 8, 4, 128, True, 11, 4),
     (41300, 64, 3, 1, 128, False, 0, 0),
+    # 16 feature tiles x 16 full token tiles fill a 256-CU chip exactly, so the ragged last
+    # token rows (64 and 100) go to the second launch of 128-token tiles
+    (4160, 64, 16, 8, 128, True, 3, 2),
+    (4196, 64, 32, 16, 64, False, 0, 0),
 ]
 
 
