@@ -31,7 +31,7 @@ from gpu_common import GRAD_C_RSS, GRAD_C_SUM, grad_errors, grad_within_bound, h
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # m, hq, hkv, d, bias, gapped positions
+    # m, hq, hkv, d, bias, gapped positions ("top": gapped, near the int32 limit)
     (1, 4, 2, 64, True, False),
     (37, 4, 4, 64, True, True),
     (100, 8, 2, 128, True, False),
@@ -40,6 +40,7 @@ CASES = [
     (600, 6, 3, 64, True, False),
     (1088, 16, 8, 128, True, False),   # the 16k needle workload's kept rows (1024 + 64 question)
     (4224, 16, 8, 128, True, False),   # the 32k multi-document workload's kept rows (4096 + 128)
+    (200, 4, 2, 128, True, "top"),     # positions within 10^6 of the int32 limit
 ]
 
 
@@ -47,7 +48,10 @@ def _case_inputs(m, hq, hkv, d, gapped, seed):
     g = np.random.default_rng(seed)
     bf = lambda shape: inputs.f32_to_bf16_bits(g.normal(size=shape).astype(np.float32))
     q, k, v, dout = bf((m, hq, d)), bf((m, hkv, d)), bf((m, hkv, d)), bf((m, hq, d))
-    pos = (np.sort(g.choice(5 * m + 3, m, replace=False)) if gapped else np.arange(m)).astype(np.int32)
+    if gapped == "top":
+        pos = np.sort(g.choice(np.arange(2**31 - 10**6, 2**31 - 1), m, replace=False)).astype(np.int32)
+    else:
+        pos = (np.sort(g.choice(5 * m + 3, m, replace=False)) if gapped else np.arange(m)).astype(np.int32)
     s = (g.normal(size=m) * 2).astype(np.float32)
     gain = g.uniform(0.5, 1.5, size=hq).astype(np.float32)
     return q, k, v, dout, pos, s, gain

@@ -196,6 +196,33 @@ def test_attention_shapes(case):
     assert err.max() <= ATTN_MAX_TOL[dtype] and err.mean() <= ATTN_MEAN_TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_positions_near_int32_max(dtype):
+    """Gapped positions within 10^6 of the int32 limit: the causal mask compares them as
+    int32 (no overflow in the kernels' position handling)."""
+    binding = require_gpu()
+    import torch
+    m, hq, hkv, d = 333, 8, 2, 128 if dtype == "bf16" else 64
+    g = np.random.default_rng(2**31 - 1)
+    store = (lambda a: inputs.f32_to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a.astype(np.float32))
+    q = store(g.normal(size=(m, hq, d)).astype(np.float32))
+    k = store(g.normal(size=(m, hkv, d)).astype(np.float32))
+    v = store(g.normal(size=(m, hkv, d)).astype(np.float32))
+    pos = np.sort(g.choice(np.arange(2**31 - 10**6, 2**31 - 1), m, replace=False)).astype(np.int32)
+    s = (g.normal(size=m) * 2).astype(np.float32)
+    gain = g.uniform(0.5, 1.5, size=hq).astype(np.float32)
+    log(f"[attention {dtype}, positions near 2^31] m={m} hq={hq} hkv={hkv} d={d} pos {pos[0]}..{pos[-1]}")
+    o = binding.tg_gated_attention(binding.to_device(q, dtype), binding.to_device(k, dtype),
+                                   binding.to_device(v, dtype), torch.from_numpy(pos).cuda(),
+                                   torch.from_numpy(s).cuda(), torch.from_numpy(gain).cuda(), 1.05)
+    torch.cuda.synchronize()
+    ref = oracle.gated_attention(inputs.to_f64(q, dtype), inputs.to_f64(k, dtype), inputs.to_f64(v, dtype), pos,
+                                 s, gain, 1.05)
+    err = np.abs(host_f64(o) - ref)
+    log(f"  max_abs={err.max():.3e} mean_abs={err.mean():.3e}")
+    assert err.max() <= ATTN_MAX_TOL[dtype] and err.mean() <= ATTN_MEAN_TOL[dtype]
+
+
 def test_attention_first_row_is_its_own_value():
     """Row 0 sees one key, so its output is V_0 rounded -- exact on the GPU too."""
     binding = require_gpu()
