@@ -82,6 +82,26 @@ __device__ __forceinline__ void bwd_dma_tile(uint32_t dst, const uint16_t* __res
   }
 }
 
+// The same DMA for a tile with no row past m: instruction I = I0 + waves j reads rows RPI I ..,
+// whose swizzle repeats every 16 rows, so one per-lane offset (tile_dma_off, formed once per
+// kernel) serves every instruction of the wave, the rows stepping through the scalar base.
+template <int D>
+__device__ __forceinline__ uint32_t tile_dma_off(int64_t ld, int I0, int lane) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
+  const int r = RPI * I0 + lane / CPR;
+  return (uint32_t)(((int64_t)r * ld + 8 * ((lane % CPR) ^ bwd_swz<D>(r))) * 2);
+}
+template <int D>
+__device__ __forceinline__ void bwd_dma_tile_full(uint32_t dst, const uint16_t* __restrict__ src, int64_t ld, int first,
+                                                  int rows, int I0, int waves, uint32_t off) {
+  constexpr int CPR = D / 8, RPI = 64 / CPR;
+  static_assert((RPI * 4) % 16 == 0, "the swizzle repeats across a wave's instructions");
+  const int n_inst = rows / RPI;
+  const char* base = reinterpret_cast<const char*>(src + (int64_t)first * ld);
+  for (int I = I0; I < n_inst; I += waves)
+    dma_lds16(off, base + (int64_t)(RPI * (I - I0)) * ld * 2, dst + I * 1024);
+}
+
 // Operand reads at a precomputed per-lane byte offset from a tile's LDS base: the offsets of
 // the swizzled layouts depend only on the lane and the k-step or d tile, so they are formed
 // once per kernel and every read is one base + offset address (plus an immediate).
@@ -213,11 +233,18 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
   const uint16_t* vh = v + (int64_t)kvh * D;
   const int64_t ld = (int64_t)hkv * D;
 
+  const int iv0 = (wave + 2) % kDqWaves;
+  const uint32_t offk = tile_dma_off<D>(ld, wave, lane), offv = tile_dma_off<D>(ld, iv0, lane);
   auto issue = [&](int t) {
     const int kb = t * kDqKeys;
     const uint32_t buf = lds0 + (t & 1) * L::BUF;
-    bwd_dma_tile<D>(buf + L::K0, kh, ld, kb, m, kDqKeys, wave, kDqWaves, lane);
-    bwd_dma_tile<D>(buf + L::V0, vh, ld, kb, m, kDqKeys, (wave + 2) % kDqWaves, kDqWaves, lane);
+    if (kb + kDqKeys <= m) {
+      bwd_dma_tile_full<D>(buf + L::K0, kh, ld, kb, kDqKeys, wave, kDqWaves, offk);
+      bwd_dma_tile_full<D>(buf + L::V0, vh, ld, kb, kDqKeys, iv0, kDqWaves, offv);
+    } else {
+      bwd_dma_tile<D>(buf + L::K0, kh, ld, kb, m, kDqKeys, wave, kDqWaves, lane);
+      bwd_dma_tile<D>(buf + L::V0, vh, ld, kb, m, kDqKeys, iv0, kDqWaves, lane);
+    }
     const uint32_t off = (uint32_t)((min(kb + lane, m - 1) - kb) * 4);
     if (wave == 0 && s_kept) dma_lds4(off, s_kept + kb, buf + L::S0);
     if (wave == 1 && pos) dma_lds4(off, pos + kb, buf + L::P0);
@@ -395,13 +422,37 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
   static_assert(PER16 >= 1 && (2 * (kDkvRows * D * 2 / 1024)) % kDkvWaves == 0, "tile DMAs split evenly");
   const bool extra = wave == 0 || (wave == 1 && pos);
 
-  auto issue = [&](int it) {
-    const int hh = it / per_head, t = first_tile + it % per_head;
+  // this wave's Q and dO pieces of a whole tile: instruction I of bwd_dma_tile (at most one
+  // per wave and matrix), its per-lane byte offset formed once; ragged tiles clamp per call
+  constexpr int CPR = D / 8, RPI = 64 / CPR, NI = kDkvRows / RPI;
+  static_assert(NI <= kDkvWaves, "one DMA per wave and matrix");
+  const int iq = wave, io = (wave + kDkvWaves / 2) % kDkvWaves;
+  auto piece_off = [&](int I) {
+    const int r = RPI * I + lane / CPR;
+    return (uint32_t)(((int64_t)r * ld + 8 * ((lane % CPR) ^ bwd_swz<D>(r))) * 2);
+  };
+  const uint32_t offq = piece_off(iq), offo = piece_off(io);
+  // tiles in issue order: it = hh per_head + (t - first_tile); counters advanced one tile at a
+  // time instead of dividing by per_head
+  auto advance = [&](int& hh, int& t) {
+    if (++t == n_qt) {
+      t = first_tile;
+      ++hh;
+    }
+  };
+  auto issue = [&](int it, int hh, int t) {
     const int head = kvh * group + hh, qb = t * kDkvRows;
     const uint32_t buf = lds0 + (it % kDkvStages) * L::BUF;
-    bwd_dma_tile<D>(buf + L::Q0, q + (int64_t)head * D, ld, qb, m, kDkvRows, wave, kDkvWaves, lane);
-    bwd_dma_tile<D>(buf + L::O0, dout + (int64_t)head * D, ld, qb, m, kDkvRows, (wave + kDkvWaves / 2) % kDkvWaves,
-                    kDkvWaves, lane);
+    if (qb + kDkvRows <= m) {
+      const char* qg = reinterpret_cast<const char*>(q + (int64_t)head * D + (int64_t)qb * ld);
+      const char* og = reinterpret_cast<const char*>(dout + (int64_t)head * D + (int64_t)qb * ld);
+      if (iq < NI) dma_lds16(offq, qg, buf + L::Q0 + iq * 1024);
+      if (io < NI) dma_lds16(offo, og, buf + L::O0 + io * 1024);
+    } else {
+      bwd_dma_tile<D>(buf + L::Q0, q + (int64_t)head * D, ld, qb, m, kDkvRows, wave, kDkvWaves, lane);
+      bwd_dma_tile<D>(buf + L::O0, dout + (int64_t)head * D, ld, qb, m, kDkvRows, (wave + kDkvWaves / 2) % kDkvWaves,
+                      kDkvWaves, lane);
+    }
     const int qi = min(qb + (lane & 31), m - 1);
     if (wave == 0) {   // lanes 0..31: lse2[head][qi], lanes 32..63: D[head][qi]
       const uint32_t off = (uint32_t)(((int64_t)head * m + qi) * 4 + (lane >= 32 ? dsum_off : 0));
@@ -410,14 +461,20 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
     if (wave == 1 && pos) dma_lds4((uint32_t)(qi * 4), pos, buf + L::ST0 + 2 * kDkvRows * 4);
   };
 
+  int ihh = 0, it_t = first_tile;   // the next tile to issue
   for (int i = 0; i < kDkvStages - 1; ++i)
-    if (i < n_it) issue(i);
+    if (i < n_it) {
+      issue(i, ihh, it_t);
+      advance(ihh, it_t);
+    }
+  int shh = 0, st_t = first_tile;   // the next tile to compute
   float col = 0.f;   // this lane's part of the sum over queries of dZ, current head
   // one query tile; ST = it mod kDkvStages is a compile-time constant, so the tile's LDS base
   // and every operand address within it are a per-lane offset plus an immediate
   auto step = [&](int it, auto stc) {
     constexpr int ST = decltype(stc)::value;
-    const int hh = it / per_head, t = first_tile + it % per_head;
+    const int hh = shh, t = st_t;
+    advance(shh, st_t);
     const int head = kvh * group + hh, qb = t * kDkvRows;
     // tile it has landed once the DMAs of the later tiles already issued are all that remain
     const int later = min(kDkvStages - 2, n_it - 1 - it);
@@ -428,7 +485,10 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       dma_wait_all();
     }
     __syncthreads();   // tile it visible to every wave; the buffer of tile it - 1 is free
-    if (it + kDkvStages - 1 < n_it) issue(it + kDkvStages - 1);
+    if (it + kDkvStages - 1 < n_it) {
+      issue(it + kDkvStages - 1, ihh, it_t);
+      advance(ihh, it_t);
+    }
     if (qb + kDkvRows - 1 >= kw0 && kw0 < m) {   // some query of the tile sees these keys
       const char* buf = lds + ST * L::BUF;   // ST = it mod kDkvStages, a constant here
       const uint16_t* q_t = reinterpret_cast<const uint16_t*>(buf + L::Q0);
