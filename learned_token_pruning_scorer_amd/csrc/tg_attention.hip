@@ -37,9 +37,9 @@
 //    exceeds it by more than 8 in the base-2 exponent, so P stays below 2^8 and most
 //    tiles skip the O rescale;
 //  * operand reads are issued ahead of the work that waits on them: the first two
-//    k-steps' K operands before the next tile's DMA, the V^T operands of the first
-//    16 keys (every d tile) before the softmax, each next 16 keys' while the
-//    current ones' products run;
+//    k-steps' K operands before the next tile's DMA, every later k-step's two k-steps
+//    before its products, the V^T operands of the first 16 keys (every d tile) before
+//    the softmax, each next 16 keys' while the current ones' products run;
 //  * the softmax and the P . V products alternate per 16 keys: the exponentials of
 //    keys 16 (s + 1) .. 16 s + 31 are issued while the four O tiles' products of the
 //    previous 16 keys run (each O tile still accumulates the keys in order);
@@ -297,12 +297,25 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
     __builtin_amdgcn_s_setprio(0);   // MFMA phase: yield issue slots to a wave in its softmax
+    // K operands in a ring of three k-steps, each read two k-steps before its products; the
+    // scheduling groups stop the compiler from sinking the reads next to their use
+    bf16x8 kr[3][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) { kr[0][kt] = kpre[0][kt]; kr[1][kt] = kpre[1][kt]; }
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
+      if (s + 2 < D / 16) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a = s < KPRE ? kpre[s < KPRE ? s : 0][kt] : read_k(s, kt, bufc);
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
+        for (int kt = 0; kt < 2; ++kt) kr[(s + 2) % 3][kt] = read_k(s + 2, kt, bufc);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[s % 3][kt], qf[s], sacc[kt], 0, 0, 0);
+      if (s + 2 < D / 16) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // then two MFMAs
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
     }
 #pragma unroll
