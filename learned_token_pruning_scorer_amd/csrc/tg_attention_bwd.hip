@@ -602,9 +602,9 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
 
 // ---------------------------------------------------------------------------------
 // Fixed-order sums of the partials.  Blocks 0 .. ceil(m/256)-1 sum ds over the
-// key/value heads; the last block sums dgain (one wave per head) and dtau (the whole
-// block).  Each sum's order is fixed by the launch shape alone, so results are
-// bitwise reproducible.
+// key/value heads, the next hq blocks dgain (one head each), the last block dtau.
+// Each sum's order is fixed by the launch shape alone, so results are bitwise
+// reproducible.
 // ---------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(int m, int hq, int hkv, int n_kblocks, int n_dkv_blocks,
                                                           const float* __restrict__ ds_part,
@@ -612,7 +612,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(int m, int hq, int hkv,
                                                           const float* __restrict__ dtau_part, float dtau_scale,
                                                           float* __restrict__ ds, float* __restrict__ dgain,
                                                           float* __restrict__ dtau) {
-  __shared__ float red[256];
+  __shared__ float red[4];
   const int n_ds_blocks = (m + 255) / 256;
   if ((int)blockIdx.x < n_ds_blocks) {
     const int j = blockIdx.x * 256 + threadIdx.x;
@@ -623,26 +623,30 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(int m, int hq, int hkv,
     }
     return;
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int per_head = n_kblocks * kDkvWaves;
-  if (dgain)
-    for (int h = wave; h < hq; h += 4) {
-      float acc = 0.f;
-      for (int i = lane; i < per_head; i += 64) acc += dgain_part[(int64_t)h * per_head + i];
+  const int b = (int)blockIdx.x - n_ds_blocks;
+  const bool is_gain = b < hq;
+  if (is_gain ? !dgain : !dtau) return;   // uniform over the block
+  const float* src = is_gain ? dgain_part + (int64_t)b * n_kblocks * kDkvWaves : dtau_part;
+  const int n = (is_gain ? n_kblocks : n_dkv_blocks) * kDkvWaves;
+  // four independent partial sums per thread, so that four loads are in flight at once
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  int i = threadIdx.x;
+  for (; i + 768 < n; i += 1024) {
+    a0 += src[i];
+    a1 += src[i + 256];
+    a2 += src[i + 512];
+    a3 += src[i + 768];
+  }
+  for (; i < n; i += 256) a0 += src[i];
+  float acc = (a0 + a1) + (a2 + a3);
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-      if (lane == 0) dgain[h] = acc;
-    }
-  if (dtau) {
-    float acc = 0.f;
-    for (int i = threadIdx.x; i < n_dkv_blocks * kDkvWaves; i += 256) acc += dtau_part[i];
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-      if ((int)threadIdx.x < s) red[threadIdx.x] += red[threadIdx.x + s];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0) *dtau = red[0] * dtau_scale;
+  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    if (is_gain) dgain[b] = tot;
+    else *dtau = tot * dtau_scale;
   }
 }
 
@@ -708,7 +712,7 @@ static tg_status attention_backward(int m, int hq, int hkv, const void* q, const
                      n_kblocks);
   // dtau = -(1/tau) sum dZ (q.k / (sqrt(d) tau)); the kernel summed dZ q.k
   const float dtau_scale = static_cast<float>(-1.0 / (sd * (double)tau));
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((m + 255) / 256 + 1), dim3(256), 0, st, m, hq, hkv, n_kblocks, n_dkv,
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((m + 255) / 256 + hq + 1), dim3(256), 0, st, m, hq, hkv, n_kblocks, n_dkv,
                      ds_part, dgain_part, dtau_part, dtau_scale, ds, dgain, dtau);
   TG_CHECK_LAUNCH();
   return TG_OK;
