@@ -282,6 +282,9 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
   const int n_iter = (t_end - t_begin + KS - 1) / KS;
   auto tt = [&](int j) { return tg0 + KS * j; };
 
+  // bias k-step A operand [s_hi, s_hi, s_lo, s_lo, 1, 0, 0, 0]: the constant upper half stays
+  // in registers, each tile writes the lower half
+  u32x4 ebias = {0u, 0u, 0x3f80u, 0u};
   constexpr int KPRE = 2;
   auto read_k = [&](int s, int kt, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
@@ -297,6 +300,14 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kt][i] = 0.f;
     __builtin_amdgcn_s_setprio(0);   // MFMA phase: yield issue slots to a wave in its softmax
+    // the tile's key scores (bias k-step) are read first, under the S products
+    float sr[2] = {0.f, 0.f};
+    if (BIAS) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        sr[kt] = *reinterpret_cast<const float*>(lds + 4 * l32 + (C::SB + buf * kBN * 4 + kt * 128));
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
     // K operands in a ring of three k-steps, each read two k-steps before its products; the
     // scheduling groups stop the compiler from sinking the reads next to their use
     bf16x8 kr[3][2];
@@ -322,14 +333,14 @@ __global__ __launch_bounds__(kAttnWaves * 64 * KS, 2 / KS) void attn_bf16_kernel
     for (int kt = 0; kt < 2; ++kt) {
       uint32_t hh = 0, ll = 0;
       if (BIAS) {   // the score as two bf16 parts, each in both halves of a word
-        const float sr = *reinterpret_cast<const float*>(lds + 4 * l32 + (C::SB + buf * kBN * 4 + kt * 128));
-        hh = pack_bf16x2(sr, sr);
-        ll = pack_bf16x2(sr - __uint_as_float(hh & 0xffff0000u), sr - __uint_as_float(hh & 0xffff0000u));
+        hh = pack_bf16x2(sr[kt], sr[kt]);
+        ll = pack_bf16x2(sr[kt] - __uint_as_float(hh & 0xffff0000u), sr[kt] - __uint_as_float(hh & 0xffff0000u));
       }
       // 1.0 at k = 4.  The upper lane half holds k = 8..15, where the B operand is zero, so its
       // (finite) values add nothing and need no masking.
-      const u32x4 e = {hh, ll, 0x3f80u, 0u};
-      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, e), qext, sacc[kt], 0, 0, 0);
+      ebias[0] = hh;
+      ebias[1] = ll;
+      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ebias), qext, sacc[kt], 0, 0, 0);
     }
     __builtin_amdgcn_s_setprio(2);   // vector phase (mask, max, exp, pack) goes first
     if ((kb + kBN - 1 > q0) || (kb + kBN > m)) {
