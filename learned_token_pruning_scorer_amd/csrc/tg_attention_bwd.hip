@@ -511,13 +511,21 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
         const u32x4 a4 = {p0[0], p0[1], p1[0], p1[1]};
         return __builtin_bit_cast(bf16x8, a4);
       };
+      // products n = 4 s + 2 b + (0: S from Q, 1: dP from dO), in that order; each operand is read
+      // three products ahead (a ring of four), scheduling fences keeping the reads there
+      constexpr int NP = 4 * KS, RING = 4;
+      auto opnd = [&](int n) { return lds_row(((n & 1) ? oc : qc) + ((n >> 1) & 1) * kBlk16, rowo[n >> 2]); };
+      bf16x8 ring[RING];
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+      for (int n = 0; n < RING - 1; ++n) ring[n] = opnd(n);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          sa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row(qc + b * kBlk16, rowo[s]), kf[s], sa[b], 0, 0, 0);
-          da[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_row(oc + b * kBlk16, rowo[s]), vf[s], da[b], 0, 0, 0);
-        }
+      for (int n = 0; n < NP; ++n) {
+        const int sk_ = n >> 2, b = (n >> 1) & 1;
+        if (n + RING - 1 < NP) ring[(n + RING - 1) % RING] = opnd(n + RING - 1);
+        if (n & 1) da[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[n % RING], vf[sk_], da[b], 0, 0, 0);
+        else sa[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ring[n % RING], kf[sk_], sa[b], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);   // one read and one product per slot, in this order
+      }
       // register i of block b holds query qb + 16 b + 4 G + i, key = this lane's.  The mask is
       // needed only where a query may precede a key of this wave or a key or query lies past
       // the end; elsewhere every pair is visible (uniform over the wave).
@@ -543,9 +551,18 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       if (masked) probs(std::true_type{});
       else probs(std::false_type{});
       const bf16x8 pb = pack8(p[0], p[1]);
+      // dV products t2 = 0 .. DT-1 then dK products: operands (transposed dO, then Q) read three
+      // products ahead in a ring of four, across the two
+      bf16x8 tring[RING];
+      auto topnd = [&](int n) { return n < DT ? tr_a(oc, n) : tr_a(qc, n - DT); };
 #pragma unroll
-      for (int t2 = 0; t2 < DT; ++t2)
-        dva[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_a(oc, t2), pb, dva[t2], 0, 0, 0);
+      for (int n = 0; n < RING - 1; ++n) tring[n] = topnd(n);
+#pragma unroll
+      for (int t2 = 0; t2 < DT; ++t2) {
+        tring[(t2 + RING - 1) % RING] = topnd(t2 + RING - 1);
+        dva[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tring[t2 % RING], pb, dva[t2], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(&d_t[16 * b + 4 * grp]);
@@ -559,8 +576,12 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       }
       const bf16x8 zb = pack8(da[0], da[1]);
 #pragma unroll
-      for (int t2 = 0; t2 < DT; ++t2)
-        dka[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_a(qc, t2), zb, dka[t2], 0, 0, 0);
+      for (int t2 = 0; t2 < DT; ++t2) {
+        const int n = DT + t2;
+        if (n + RING - 1 < 2 * DT) tring[(n + RING - 1) % RING] = topnd(n + RING - 1);
+        dka[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tring[n % RING], zb, dka[t2], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     if (t == n_qt - 1) {
       // this head's key-side sums: the four lane groups hold parts of the same key's column
