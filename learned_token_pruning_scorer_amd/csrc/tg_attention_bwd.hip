@@ -264,10 +264,19 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
     f32x16 sa, da;
 #pragma unroll
     for (int i = 0; i < 16; ++i) { sa[i] = 0.f; da[i] = 0.f; }
+    // products n = 2 s + (0: S^T from K, 1: dP^T from V), in that order; each operand is read
+    // RING - 1 products ahead in a ring, scheduling fences keeping the reads there
+    constexpr int NP = 2 * (D / 16), RING = 3;
+    auto opnd = [&](int n) { return lds_row((n & 1) ? vh2 : kh2, rowo[n >> 1]); };
+    bf16x8 ring[RING];
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(kh2, rowo[s]), qf[s], sa, 0, 0, 0);
-      da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row(vh2, rowo[s]), df[s], da, 0, 0, 0);
+    for (int n = 0; n < RING - 1; ++n) ring[n] = opnd(n);
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+      if (n + RING - 1 < NP) ring[(n + RING - 1) % RING] = opnd(n + RING - 1);
+      if (n & 1) da = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % RING], df[n >> 1], da, 0, 0, 0);
+      else sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % RING], qf[n >> 1], sa, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // register e holds key kb2 + 8 (e/4) + 4 half + e%4, query = this lane's row.  The mask
     // is needed only where a key may follow a query (positions rise with the index) or a key
@@ -296,16 +305,24 @@ __global__ __launch_bounds__(kDqWaves * 64, 2) void bwd_dq_kernel(
     if (masked) dz(std::true_type{});
     else dz(std::false_type{});
     const bf16x8 z0 = pack_acc(da, 0), z1 = pack_acc(da, 1);
+    // dQ products n = 2 u + s2 (keys 16 s2 .. 16 s2 + 15 of the half), K^T operands read
+    // RING - 1 products ahead
+    auto kt_opnd = [&](int n) {
+      const int u = n >> 1, s2 = n & 1;
+      const u32x2 p0 = lds_tr(kh2 + s2 * 16 * D * 2, tro[u][0]);
+      const u32x2 p1 = lds_tr(kh2 + s2 * 16 * D * 2, tro[u][1]);
+      const u32x4 a4 = {p0[0], p0[1], p1[0], p1[1]};
+      return __builtin_bit_cast(bf16x8, a4);
+    };
+    constexpr int NQ = 2 * (D / 32);
 #pragma unroll
-    for (int u = 0; u < D / 32; ++u)
+    for (int n = 0; n < RING - 1; ++n) ring[n] = kt_opnd(n);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {   // keys 16 s2 .. 16 s2 + 15 of the half
-        const u32x2 p0 = lds_tr(kh2 + s2 * 16 * D * 2, tro[u][0]);
-        const u32x2 p1 = lds_tr(kh2 + s2 * 16 * D * 2, tro[u][1]);
-        const u32x4 a4 = {p0[0], p0[1], p1[0], p1[1]};
-        dqa[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4), s2 == 0 ? z0 : z1, dqa[u],
-                                                         0, 0, 0);
-      }
+    for (int n = 0; n < NQ; ++n) {
+      if (n + RING - 1 < NQ) ring[(n + RING - 1) % RING] = kt_opnd(n + RING - 1);
+      dqa[n >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[n % RING], (n & 1) ? z1 : z0, dqa[n >> 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   auto step = [&](int t, auto bufc) {
     const int kb = t * kDqKeys;
