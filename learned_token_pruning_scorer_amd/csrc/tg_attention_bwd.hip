@@ -535,6 +535,13 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       bf16x8 ring[RING];
 #pragma unroll
       for (int n = 0; n < RING - 1; ++n) ring[n] = opnd(n);
+      // the rows' statistics (lse in base-2 units, D) are read with the first operands
+      f32x4_t lvs[2], dvs[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        lvs[b] = *reinterpret_cast<const f32x4_t*>(&lse_t[16 * b + 4 * grp]);
+        dvs[b] = *reinterpret_cast<const f32x4_t*>(&d_t[16 * b + 4 * grp]);
+      }
 #pragma unroll
       for (int n = 0; n < NP; ++n) {
         const int sk_ = n >> 2, b = (n >> 1) & 1;
@@ -552,7 +559,7 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const int i0 = 16 * b + 4 * grp;
-          const f32x4_t lv = *reinterpret_cast<const f32x4_t*>(&lse_t[i0]);
+          const f32x4_t lv = lvs[b];
           i32x4 qp = {};
           if (decltype(maskc)::value) {
             if (pos) qp = *reinterpret_cast<const i32x4*>(&p_t[i0]);
@@ -582,7 +589,7 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const f32x4_t dv4 = *reinterpret_cast<const f32x4_t*>(&d_t[16 * b + 4 * grp]);
+        const f32x4_t dv4 = dvs[b];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float z = p[b][i] * (da[b][i] - dv4[i]);
