@@ -354,20 +354,28 @@ __global__ __launch_bounds__(kScoreWaves * 64, 1) void score_ring_kernel(
     __syncthreads();   // chunk c visible to all waves; chunk c - 1's slot free for reuse
     if (c + NS - 1 < nch) issue(c + NS - 1, (slot + NS - 1) % NS);
     const char* st = ring + slot * T::STAGE;
-#pragma unroll
-    for (int ks = 0; ks < kRingKC / 16; ++ks) {
-      bf16x8 af[AT], bfr[BTW];
+    // operands of k-step ks + 1 are read before the products of k-step ks (two register sets),
+    // scheduling fences keeping them there
+    constexpr int NKS = kRingKC / 16;
+    bf16x8 af[2][AT], bfr[2][BTW];
+    auto load = [&](int ks, int buf) {
 #pragma unroll
       for (int a = 0; a < AT; ++a)
-        af[a] = *reinterpret_cast<const bf16x8*>(st + oa[ks] + 32 * kRingRow * (wh * AT + a));
+        af[buf][a] = *reinterpret_cast<const bf16x8*>(st + oa[ks] + 32 * kRingRow * (wh * AT + a));
 #pragma unroll
       for (int b = 0; b < BTW; ++b)
-        bfr[b] = *reinterpret_cast<const bf16x8*>(st + T::WB + oa[ks] + 32 * kRingRow * (wt * BTW + b));
+        bfr[buf][b] = *reinterpret_cast<const bf16x8*>(st + T::WB + oa[ks] + 32 * kRingRow * (wt * BTW + b));
+    };
+    load(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 1 < NKS) load(ks + 1, (ks + 1) & 1);
 #pragma unroll
       for (int a = 0; a < AT; ++a)
 #pragma unroll
         for (int b = 0; b < BTW; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][a], bfr[ks & 1][b], acc[a][b], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   for (int c = 0; c < nch; c += NS) {   // unrolled by NS so the stage slot is a constant
