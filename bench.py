@@ -42,9 +42,9 @@ STAGES = ("score", "select", "gather", "attention")   # the step's launches, in 
 # HBM bytes per launch of the attention kernel on long128k, from rocprofv3 FETCH_SIZE and WRITE_SIZE
 # scaled by the same counters' reading of the calibration copy (profiles/long128k_hbm_counters.md).
 # Reported only while the kernel source is the one the counters were taken on.
-ATTN_TRAFFIC = {"workload": "long128k", "bytes": 116424488,
+ATTN_TRAFFIC = {"workload": "long128k", "bytes": 116849680,
                 "source": "learned_token_pruning_scorer_amd/csrc/tg_attention.hip",
-                "sha256": "0c6e98c459374f6243026eb414a0b563576fd8cd8afa44a3acc16286d59ee505"}
+                "sha256": "4b3e2e9612150eb779f62a79a73930e8f5637608f32ae5872c4946d393a8b659"}
 
 
 def parse():
