@@ -583,7 +583,7 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       for (int n = 0; n < RING - 1; ++n) tring[n] = topnd(n);
 #pragma unroll
       for (int t2 = 0; t2 < DT; ++t2) {
-        tring[(t2 + RING - 1) % RING] = topnd(t2 + RING - 1);
+        if (t2 + RING - 1 < 2 * DT) tring[(t2 + RING - 1) % RING] = topnd(t2 + RING - 1);
         dva[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tring[t2 % RING], pb, dva[t2], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
