@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bwd_dkv_kernel(
       };
       // products n = 4 s + 2 b + (0: S from Q, 1: dP from dO), in that order; each operand is read
       // three products ahead (a ring of four), scheduling fences keeping the reads there
-      constexpr int NP = 4 * KS, RING = 4;
+      constexpr int NP = 4 * KS, RING = 5;
       auto opnd = [&](int n) { return lds_row(((n & 1) ? oc : qc) + ((n >> 1) & 1) * kBlk16, rowo[n >> 2]); };
       bf16x8 ring[RING];
 #pragma unroll
