@@ -37,6 +37,11 @@ def _select_cases():
     cases.append(("normal-16384", g.normal(size=16384), 0, 16320, [1024, 16319]))
     cases.append(("ragged-16385", g.normal(size=16385), 3, 16385, [5, 8000]))
     cases.append(("all-equal-20000", np.full(20000, -1.5), 100, 19900, [1, 9999, 19799]))
+    # sizes just past 4096, 8192 and 32768 positions (partly filled last chunk rounds)
+    cases.append(("ragged-4097", g.normal(size=4097), 0, 4097, [1, 2048, 4096]))
+    cases.append(("ragged-8193", g.normal(size=8193), 100, 8100, [1, 4000, 7999]))
+    cases.append(("ragged-32767", np.round(g.normal(size=32767) * 16) / 16, 0, 32700, [1, 16000, 32699]))
+    cases.append(("ragged-32769", g.normal(size=32769), 0, 32769, [1, 4096, 32768]))
     # more positions than 64 chunks hold in registers: keys are re-read in every pass
     cases.append(("beyond-registers-140001", g.normal(size=140001), 0, 139000, [1, 4096, 100000]))
     return cases
@@ -54,6 +59,26 @@ def test_select_edge_cases(case):
         kept = binding.tg_select_topk(s32, b, e, k)
         binding.tg_select_check(binding.select_workspace(len(s), "cuda"))
         assert np.array_equal(kept.cpu().numpy().astype(np.int64), oracle.select_topk(s_exact, b, e, k))
+
+
+@pytest.mark.parametrize("n", [3000, 16384, 32768])
+def test_select_unaligned_scores(n):
+    """Scores that start 4 bytes past a 16-byte boundary select the same positions as the
+    oracle; random-K at the same sizes and spans too."""
+    binding = require_gpu()
+    import torch
+    g = np.random.default_rng(n)
+    s = np.round(g.normal(size=n) * 32) / 32
+    buf = torch.from_numpy(np.concatenate([[0.0], s]).astype(np.float32)).cuda()
+    s32 = buf[1:]
+    assert s32.data_ptr() % 16 == 4
+    for b, e, k in ((0, n - 64, n // 16), (7, n, 1), (n // 3, 2 * n // 3, n // 10)):
+        log(f"[select unaligned] n={n} doc=[{b},{e}) k={k}")
+        kept = binding.tg_select_topk(s32, b, e, k)
+        binding.tg_select_check(binding.select_workspace(n, "cuda"))
+        assert np.array_equal(kept.cpu().numpy().astype(np.int64), oracle.select_topk(s, b, e, k))
+        rk = binding.tg_select_random(n, b, e, k, seed=n + k)
+        assert np.array_equal(rk.cpu().numpy().astype(np.int64), oracle.select_random(n, b, e, k, n + k))
 
 
 def test_select_workspace_reuse_across_sizes():
