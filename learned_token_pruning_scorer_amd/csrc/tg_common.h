@@ -90,6 +90,13 @@ __device__ __forceinline__ void dma_lds16(uint32_t off, const void* base, uint32
                : "=&s"(save) : "s"(m0v), "v"(off), "s"(base) : "memory");
 }
 
+// The same with the non-temporal cache policy, for data read exactly once.
+__device__ __forceinline__ void dma_lds16_nt(uint32_t off, const void* base, uint32_t m0v) {
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3 nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "s"(m0v), "v"(off), "s"(base) : "memory");
+}
+
 // The same for 4 bytes per lane (global_load_lds_dword): LDS byte m0v + 4 L.
 __device__ __forceinline__ void dma_lds4(uint32_t off, const void* base, uint32_t m0v) {
   uint32_t save;
