@@ -8,9 +8,7 @@
 // the stores, so one 4 KiB row (d_model 2048, bf16) is one load per thread.  8 rows per
 // workgroup from 8192 rows on (half the workgroups, twice the bytes in flight per thread;
 // at M = 8256 the 4-row grid, 2064 workgroups of 256 threads, is 16 more than the chip
-// holds at once), 4 below, where more workgroups spread the rows over more CUs.  The source
-// rows are read once, with non-temporal loads (15.8 -> 13.7 us per launch at 8256 rows of
-// 4 KiB); the output is stored normally, so it stays cached for the layer that reads it next.
+// holds at once), 4 below, where more workgroups spread the rows over more CUs.
 #include "tg_common.h"
 
 namespace tg {
@@ -35,7 +33,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_vec16_kernel(
     u32x4 v[ROWS];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r)
-      if (live[r]) v[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + (int64_t)src[r] * ldx_bytes + 16 * (int64_t)p));
+      if (live[r]) v[r] = *reinterpret_cast<const u32x4*>(x + (int64_t)src[r] * ldx_bytes + 16 * (int64_t)p);
 #pragma unroll
     for (int r = 0; r < ROWS; ++r)
       if (live[r]) *reinterpret_cast<u32x4*>(out + (int64_t)(r0 + r) * ldo_bytes + 16 * (int64_t)p) = v[r];
